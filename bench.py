@@ -1,0 +1,198 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X MegaMoE per-rank layer forward (one GPU).
+
+A step is one pass of the whole path over one batch of received rows:
+stage (BF16 -> e4m3 1x128 quantisation + route check) -> compaction ->
+FC1 (+ SwiGLU + 1x128 requant) -> FC2 -> weighted combine to BF16.  Inputs
+are synthetic and already resident in HBM when timing starts.
+
+Default workload: the DeepSeek-V3-like one-GPU share (H=7168, I=2048, 32
+local experts, top-8, balanced block-permutation routing, T=4096 tokens).
+
+Prints one JSON line: TFLOP/s of the whole step (GEMM FLOPs 6*R*H*I), the
+roofline of the dominant kernel (FC1, timed with HIP events on its launch
+stream inside the library) and the float64 CPU oracle timed on a bounded
+sample of the same workload on this host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (no sparsity)
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def workload_bytes(shape, counts, tokens, with_stage=True):
+    """Algorithmic HBM bytes of one step (see the design notes for each term)."""
+    H, I = shape.hidden, shape.intermediate
+    R = int(sum(counts))
+    touched = int(sum(1 for c in counts if c > 0))
+    w = touched * (2 * I * H + H * I + 4 * ((2 * I // 128) * (H // 128) + (H // 128) * (I // 128)))
+    x = tokens * H + tokens * H // 32               # e4m3 rows + scales read by FC1
+    h = 2 * R * I * (1 + 4 / 128)                   # e4m3 h + scales, write + read
+    y = 2 * R * H * 2                               # bf16 y, write + read
+    out = tokens * H * 2
+    meta = R * 16
+    stage = (2 * tokens * H + tokens * H + tokens * H // 32) if with_stage else 0
+    return w + x + h + y + out + meta + stage
+
+
+def fc1_flops(R, H, I):
+    return 4.0 * R * H * I
+
+
+def run_cpu_baseline(inp, sample_tokens):
+    """The float64 oracle, as it stands, on the first `sample_tokens` tokens."""
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    from oracle import moe_ref
+
+    S = sample_tokens
+    t0 = time.perf_counter()
+    moe_ref.forward_fp8(inp.x_bf16[:S], inp.topk_idx[:S], inp.topk_w[:S], inp.w13, inp.w13_scale, inp.w2,
+                        inp.w2_scale)
+    dt = time.perf_counter() - t0
+    R = S * inp.shape.top_k
+    flops = 6.0 * R * inp.shape.hidden * inp.shape.intermediate
+    cores = min(threads, len(os.sched_getaffinity(0)))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {S} of {inp.shape.tokens} tokens of the same workload (full forward incl. "
+                      f"staging and weight decode), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="dsv3", choices=["tiny", "small", "dsv3", "skewed"])
+    ap.add_argument("--tokens", type=int, default=None, help="override T (token sweep)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-sample", type=int, default=384, help="tokens for the CPU oracle baseline (0: skip)")
+    ap.add_argument("--sweep", default="", help="comma-separated token counts; extra lines to --sweep-out")
+    ap.add_argument("--sweep-out", default="gpurun_out/sweep.jsonl")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the layer; runs on more than one GPU are not part of "
+              "this build (the expert-parallel exchange is out of scope).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mixture_experts_ffn_route_amd.harness import make_layer, to_device
+    from synthetic import CONFIGS, MoEShape, make_layer_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    base = CONFIGS[args.config]
+
+    def measure(tokens, steps, warmup):
+        shape = MoEShape(tokens, base.hidden, base.intermediate, base.experts, base.top_k, base.routing)
+        t0 = time.perf_counter()
+        inp = make_layer_inputs(shape, seed=args.seed)
+        log(f"[bench] generated T={tokens} inputs in {time.perf_counter() - t0:.1f}s")
+        dev = to_device(inp)
+        layer = make_layer(shape, dev)
+        out = torch.empty((tokens, shape.hidden), dtype=torch.bfloat16, device="cuda")
+
+        def step():
+            layer.stage(dev.x, dev.topk_idx, dev.topk_w, out=out)
+            layer.forward()
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        layer.profile(True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        prof = layer.profile_read()
+        layer.profile(False)
+        status = layer.status()
+        counts = layer.region("counts", torch.int32, (shape.experts,)).cpu().numpy()
+        return shape, inp, layer, dt / steps, prof, status, counts
+
+    for T in [int(t) for t in args.sweep.split(",") if t]:
+        shape, _, layer, sec, prof, status, counts = measure(T, max(5, args.steps // 2), args.warmup)
+        R = int(counts.sum())
+        flops = 6.0 * R * shape.hidden * shape.intermediate
+        B = workload_bytes(shape, counts, T)
+        kern = {k: v[0] / max(v[1], 1) for k, v in prof.items()}
+        rec = {"tokens": T, "ms_per_step": sec * 1e3, "tflops": flops / sec / 1e12, "gbs": B / sec / 1e9,
+               "pct_fp8_peak": 100 * flops / sec / 1e12 / FP8_PEAK_TFLOPS, "pct_hbm_peak": 100 * B / sec / 1e9 / HBM_PEAK_GBS,
+               "kernel_ms": kern, "tactic": layer.tactic(), "status": status}
+        log("[sweep]", json.dumps(rec))
+        os.makedirs(os.path.dirname(args.sweep_out) or ".", exist_ok=True)
+        with open(args.sweep_out, "a") as f:
+            f.write(json.dumps(rec) + "\n")
+        layer.close()
+        del layer
+        torch.cuda.empty_cache()
+
+    T = args.tokens or base.tokens
+    shape, inp, layer, sec, prof, status, counts = measure(T, args.steps, args.warmup)
+    R = int(counts.sum())
+    H, I = shape.hidden, shape.intermediate
+    flops = 6.0 * R * H * I
+    B = workload_bytes(shape, counts, T)
+    fc1_ms, fc1_n = prof["fc1"]
+    fc1_avg_s = fc1_ms / max(fc1_n, 1) / 1e3
+    achieved = fc1_flops(R, H, I) / fc1_avg_s / 1e12
+    kern = {k: round(v[0] / max(v[1], 1), 4) for k, v in prof.items()}
+    log(f"[bench] T={T} R={R} status={status} ms/step={sec * 1e3:.3f} kernel avg ms={kern} tactic={layer.tactic()}")
+    log(f"[bench] step {flops / sec / 1e12:.1f} TFLOP/s, {B / sec / 1e9:.0f} GB/s algorithmic")
+
+    cpu = None
+    if args.cpu_sample > 0:
+        log(f"[bench] CPU oracle baseline on {min(args.cpu_sample, T)} tokens ...")
+        cpu = run_cpu_baseline(inp, min(args.cpu_sample, T))
+        log(f"[bench] cpu baseline {cpu}")
+
+    line = {
+        "metric": "MoE layer TFLOP/s + % FP8 MFMA peak (HBM GB/s small T), 32 experts",
+        "value": round(flops / sec / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config} T={T} H={H} I={I} E={shape.experts} K={shape.top_k} "
+                               f"routing={shape.routing}", "tokens": T, "routes": R,
+                   "hbm_gbs_algorithmic": round(B / sec / 1e9, 1),
+                   "pct_fp8_peak": round(100 * flops / sec / 1e12 / FP8_PEAK_TFLOPS, 2),
+                   "kernel_avg_ms": kern},
+        "roofline": {"bound": "mfma", "kernel": "fc1 (FP8 grouped GEMM + SwiGLU + 1x128 requant)",
+                     "achieved": round(achieved, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

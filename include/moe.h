@@ -1,0 +1,236 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MegaMoE per-rank layer forward.
+ *
+ * One GPU's share of an expert-parallel MoE layer: the rows "received" from
+ * peers are a plain device buffer, and the layer runs
+ *
+ *   stage (quantise x to e4m3 1x128, check + mask routes)
+ *   -> compact (per-expert row lists)
+ *   -> FC1 (FP8 block-scale grouped GEMM) with fused SwiGLU + 1x128 requant
+ *   -> FC2 (FP8 block-scale grouped GEMM)
+ *   -> owner-side FP32 weighted top-k combine to a BF16 output.
+ *
+ * This is the forward pipeline in the Description of "feat(moe_ep): add SM90
+ * push FP8 mega-MoE backend for Hopper" (flashinfer PR #4069) with its
+ * cross-GPU steps (tags, acks, peer dispatch, prefix waits) removed, the
+ * staging contract of "perf(moe_ep): fuse Rubin MegaMoE forward preparation"
+ * (PR #6398) and the BF16-activation x MXFP8-weight variant of
+ * "feat(moe_ep): MXFP8 x BF16 integration" (PR #4604).
+ *
+ * Conventions for every entry point:
+ *  - Device pointers are HIP device memory owned by the caller; the library
+ *    never allocates or frees device memory.  Host pointers are marked.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *    Every launch is stream-ordered; no entry point except moe_read_status
+ *    synchronises with the host.
+ *  - A negative moe_status_t is returned by synchronous host validation
+ *    before anything is launched; moe_last_error() then describes it.
+ *  - Problems found on the device (bad routes, capacity overflow) never
+ *    abort: the offending routes are masked and a bit is set in the device
+ *    status word, read with moe_read_status().
+ *  - Calls on one layer handle are not thread-safe; distinct handles with
+ *    distinct workspaces are independent.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,        /* null/misaligned pointer, bad size or value */
+  MOE_ERR_UNSUPPORTED = -2,        /* valid but unsupported configuration */
+  MOE_ERR_WORKSPACE_TOO_SMALL = -3,
+  MOE_ERR_CAPACITY = -4,           /* num_tokens > max_rows */
+  MOE_ERR_STATE = -5,              /* call out of order (forward before stage) */
+  MOE_ERR_HIP = -6                 /* a HIP runtime call failed */
+} moe_status_t;
+
+/* Weight storage formats. */
+enum {
+  /* e4m3 (OCP, max 448) codes with one float32 scale per 128x128 block --
+   * the DeepSeek-style FP8 block scaling listed in the Limitations of PR #4069. */
+  MOE_WEIGHT_E4M3_BLOCK128 = 0,
+  /* e4m3 codes with one E8M0 exponent per 32 consecutive K elements (OCP MX)
+   * -- the MXFP8 weights of PR #4604. */
+  MOE_WEIGHT_MXFP8_E4M3 = 1
+};
+
+/* Activation formats (what moe_stage_inputs receives and FC1 consumes). */
+enum {
+  MOE_ACT_E4M3_1X128 = 0,  /* e4m3 rows with one float32 scale per 128 columns */
+  MOE_ACT_BF16 = 1         /* bfloat16 rows, used as exact values (MXFP8 variant) */
+};
+
+/* cfg->flags */
+enum {
+  /* Value checks of the routing checker of PR #6398: duplicate experts within
+   * a token and non-finite weights on active routes.  Off: the caller
+   * guarantees valid routing; expert-id bounds are still enforced and masked
+   * scores still zeroed. */
+  MOE_FLAG_CHECK_ROUTES = 1u,
+  /* Stage one activation row per route instead of one per token.  Exists to
+   * show the deduplicated layout gives identical results (PR #4069,
+   * Description, deduplicated dispatch bullet); costs K times the rows. */
+  MOE_FLAG_PER_ROUTE_STAGING = 2u
+};
+
+/* Device status bits (moe_read_status). */
+enum {
+  MOE_DEV_BAD_EXPERT = 1u,   /* an expert id outside [-1, E) was masked */
+  MOE_DEV_DUPLICATE = 2u,    /* a repeated expert within a token was masked (lowest slot kept) */
+  MOE_DEV_NONFINITE = 4u,    /* an active route with a NaN/inf weight was masked */
+  MOE_DEV_CAPACITY = 8u      /* routes beyond the row capacity were dropped */
+};
+
+typedef struct {
+  int32_t hidden;         /* H, multiple of 128 */
+  int32_t intermediate;   /* I, multiple of 128 (FC1 produces 2I: gate rows then up rows) */
+  int32_t num_experts;    /* E local experts, 1..1024 */
+  int32_t top_k;          /* K in {1, 2, 4, 6, 8} (Limitations of PR #4069) */
+  int32_t weight_format;  /* MOE_WEIGHT_* */
+  int32_t act_format;     /* MOE_ACT_*: E4M3_1X128 with E4M3_BLOCK128 weights, BF16 with MXFP8 */
+  uint32_t flags;         /* MOE_FLAG_* */
+} moe_config_t;
+
+/* Static expert weights, device memory, row-major, K contiguous:
+ *   w13       e4m3 [E, 2I, H]   rows 0..I-1 gate, rows I..2I-1 up
+ *   w2        e4m3 [E, H, I]
+ *   E4M3_BLOCK128: w13_scale float32 [E, 2I/128, H/128], w2_scale float32 [E, H/128, I/128]
+ *   MXFP8_E4M3:    w13_scale uint8   [E, 2I, H/32],      w2_scale uint8   [E, H, I/32]
+ * The caller keeps them alive and unchanged while the layer handle exists. */
+typedef struct {
+  const void* w13;
+  const void* w13_scale;
+  const void* w2;
+  const void* w2_scale;
+} moe_weights_t;
+
+/* Tile tactic the library chose (informational). */
+typedef struct {
+  int32_t token_bucket;  /* clamped ceil-power-of-two of expected_m, in [8, 32768] */
+  int32_t block_m;       /* rows per GEMM tile */
+  int32_t block_n;       /* weight rows per GEMM tile */
+  int32_t grid_fc1;      /* persistent workgroups launched for FC1 */
+  int32_t grid_fc2;
+  int32_t row_cap;       /* route rows the workspace holds */
+  int32_t max_m_tiles;   /* bound on (expert, row-tile) pairs */
+  int32_t reserved;
+} moe_tactic_t;
+
+/* Workspace regions exposed for inspection (moe_layer_region). */
+enum {
+  MOE_REGION_STATUS = 0,        /* uint32 [8]: status bits, staged tokens, kept routes, m-tiles */
+  MOE_REGION_STAGED_IDX = 1,    /* int32 [max_rows*K]   expert per route, -1 masked */
+  MOE_REGION_STAGED_W = 2,      /* float32 [max_rows*K] weight per route, 0 masked */
+  MOE_REGION_XQ = 3,            /* e4m3 [rows_x, H]  (bf16 [rows_x, H] for MOE_ACT_BF16) */
+  MOE_REGION_XS = 4,            /* float32 [rows_x, H/128] (unused for MOE_ACT_BF16) */
+  MOE_REGION_COUNTS = 5,        /* int32 [E]   kept routes per expert */
+  MOE_REGION_OFFSETS = 6,       /* int32 [E+1] exclusive prefix of counts */
+  MOE_REGION_SORTED_ROUTE = 7,  /* int32 [row_cap] route ids t*K+k, expert-major, ascending in expert */
+  MOE_REGION_ROUTE_POS = 8,     /* int32 [max_rows*K] inverse of sorted_route, -1 if not kept */
+  MOE_REGION_HQ = 9,            /* FC1 output rows [row_cap, I]: e4m3 (bf16 for MXFP8) */
+  MOE_REGION_HS = 10,           /* float32 [row_cap, I/128] (FP8 path) */
+  MOE_REGION_Y = 11,            /* bf16 [row_cap, H] un-weighted FC2 rows */
+  MOE_REGION_TILES = 12         /* int32 [max_m_tiles, 2] (expert, first sorted row) */
+};
+
+/* Kernel classes timed by the optional profiler. */
+enum {
+  MOE_KERNEL_STAGE = 0,
+  MOE_KERNEL_COMPACT = 1,
+  MOE_KERNEL_FC1 = 2,
+  MOE_KERNEL_FC2 = 3,
+  MOE_KERNEL_COMBINE = 4,
+  MOE_KERNEL_COUNT = 5
+};
+
+typedef struct moe_layer moe_layer_t;
+
+/* Size of the device workspace a layer needs.  Host only, launches nothing.
+ *  expected_m      expected rows per expert; picks the tile tactic only.
+ *  max_rows        token capacity per call (bounds memory).
+ *  capacity_factor route rows held = ceil(capacity_factor * max_rows * K),
+ *                  capped at max_rows*K; 1.0 never drops a route.
+ *  ws_bytes        [host out] bytes, a multiple of 256.
+ * The split between tactic (expected_m) and memory bound (max_rows,
+ * capacity_factor) is the workspace contract of PR #4069 ("Contracts
+ * introduced by this PR": capacity_factor bounds the GEMM and scale buffers;
+ * the query takes explicit expected_m and max_rows). */
+moe_status_t moe_workspace_query(const moe_config_t* cfg, int32_t expected_m, int32_t max_rows,
+                                 float capacity_factor, size_t* ws_bytes);
+
+/* Bind the static weights and the workspace (PR #4069, Contracts: the
+ * construction of the stateful variant binds transformed static weights).
+ *  cfg, w          [host in] copied; weight pointers must stay valid.
+ *  workspace       device, 256-byte aligned, ws_bytes >= moe_workspace_query().
+ *  out             [host out] new handle (host memory owned by the library).
+ * Launches nothing: the kernels read the weights in the layout above. */
+moe_status_t moe_layer_create(const moe_config_t* cfg, int32_t expected_m, int32_t max_rows,
+                              float capacity_factor, const moe_weights_t* w, void* workspace,
+                              size_t ws_bytes, void* stream, moe_layer_t** out);
+
+/* Stage one batch of received rows and bind the output tensor
+ * (PR #4069, Contracts: stage_inputs pre-binds the caller's output tensor;
+ * PR #6398: fused input quantisation + route staging + routing checker).
+ *  x          device. act_format E4M3_1X128: either bfloat16 [T, H] with
+ *             x_scale == NULL (quantised here: s = amax/448 per 1x128 block,
+ *             q = RNE_sat(x/s)), or e4m3 [T, H] with x_scale float32
+ *             [T, H/128] (copied).  act_format BF16: bfloat16 [T, H], x_scale NULL.
+ *  topk_idx   device int32 [T, K]: expert per slot, -1 = masked slot.
+ *  topk_w     device float32 [T, K]: routing weight (ignored for masked slots).
+ *  num_tokens T, 0 <= T <= max_rows (else MOE_ERR_CAPACITY).
+ *  out_bf16   device bfloat16 [T, H], written by the next moe_layer_forward.
+ * The caller's tensors are never modified.  Rows [T, max_rows) of the staged
+ * routes are masked. */
+moe_status_t moe_stage_inputs(moe_layer_t* layer, const void* x, const float* x_scale,
+                              const int32_t* topk_idx, const float* topk_w, int32_t num_tokens,
+                              void* out_bf16, void* stream);
+
+/* Run compact -> FC1(+SwiGLU+requant) -> FC2 -> combine on the staged batch.
+ * Stream-ordered, no host synchronisation (PR #4069, Description: no
+ * host-side synchronization in the steady-state forward). */
+moe_status_t moe_layer_forward(moe_layer_t* layer, void* stream);
+
+/* Synchronise `stream` and return the device status bits (MOE_DEV_*)
+ * accumulated since the last moe_stage_inputs.  bits: [host out]. */
+moe_status_t moe_read_status(moe_layer_t* layer, void* stream, uint32_t* bits);
+
+/* Device pointer and size of a workspace region (MOE_REGION_*). */
+moe_status_t moe_layer_region(moe_layer_t* layer, int32_t region, void** dptr, size_t* bytes);
+
+/* The tactic chosen at create time. tactic: [host out]. */
+moe_status_t moe_layer_tactic(const moe_layer_t* layer, moe_tactic_t* tactic);
+
+/* Optional per-kernel timing with HIP events recorded around each launch on
+ * the launch stream.  enable != 0 starts (and resets) accumulation.
+ * moe_profile_read synchronises, then returns, per MOE_KERNEL_* class, the
+ * summed milliseconds and the number of launches timed (host arrays of
+ * MOE_KERNEL_COUNT). */
+moe_status_t moe_profile_enable(moe_layer_t* layer, int32_t enable);
+moe_status_t moe_profile_read(moe_layer_t* layer, double* ms_total, int64_t* launches);
+
+/* Release the handle (host memory only; the workspace stays the caller's).
+ * Destroying NULL is a no-op. */
+moe_status_t moe_layer_destroy(moe_layer_t* layer);
+
+/* Token bucket of the tactic table: clamped ceil power of two in
+ * [8, 32768] (test "token bucket uses clamped ceil power of two" of the SM90
+ * pull-style MegaMoE, flashinfer PR #4688).  Returns -1 for tokens <= 0. */
+int32_t moe_token_bucket(int32_t tokens);
+
+/* Static string for a status code; thread-local description of the last
+ * error of this thread (empty if none). */
+const char* moe_status_string(moe_status_t status);
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

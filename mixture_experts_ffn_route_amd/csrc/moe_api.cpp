@@ -1,0 +1,339 @@
+// Entry points of include/moe.h: handle lifecycle, staging, forward, status,
+// regions and optional per-kernel event timing.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "moe_internal.h"
+
+namespace moe {
+const char* last_error();
+void clear_error();
+}  // namespace moe
+
+struct EventPair {
+  hipEvent_t start, stop;
+  int kind;
+};
+
+struct moe_layer {
+  moe_config_t cfg;
+  moe_weights_t w;
+  moe::Tactic tac;
+  moe::Layout L;
+  uint8_t* ws;
+  int32_t max_rows;
+  int32_t expected_m;
+  float capacity_factor;
+  int32_t staged_tokens;
+  void* out;
+  int32_t grid_fc1, grid_fc2;
+  // profiling
+  bool prof;
+  std::vector<EventPair> pending;
+  std::vector<hipEvent_t> pool;
+  double ms[MOE_KERNEL_COUNT];
+  int64_t launches[MOE_KERNEL_COUNT];
+};
+
+namespace {
+
+template <typename T>
+T* region(moe_layer* l, int r) {
+  return reinterpret_cast<T*>(l->ws + l->L.off[r]);
+}
+
+hipEvent_t take_event(moe_layer* l) {
+  if (!l->pool.empty()) {
+    hipEvent_t e = l->pool.back();
+    l->pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Records a start event if profiling; returns the pending index or -1.
+int prof_begin(moe_layer* l, int kind, hipStream_t s) {
+  if (!l->prof) return -1;
+  EventPair p{take_event(l), take_event(l), kind};
+  if (!p.start || !p.stop) return -1;
+  (void)hipEventRecord(p.start, s);
+  l->pending.push_back(p);
+  return (int)l->pending.size() - 1;
+}
+
+void prof_end(moe_layer* l, int idx, hipStream_t s) {
+  if (idx >= 0) (void)hipEventRecord(l->pending[idx].stop, s);
+}
+
+moe_status_t hip_fail(const char* what) {
+  hipError_t e = hipGetLastError();
+  return moe::fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" moe_status_t moe_layer_create(const moe_config_t* cfg, int32_t expected_m, int32_t max_rows,
+                                         float capacity_factor, const moe_weights_t* w, void* workspace,
+                                         size_t ws_bytes, void* stream, moe_layer_t** out) {
+  (void)stream;
+  moe::clear_error();
+  moe_status_t s = moe::validate_config(cfg, expected_m, max_rows, capacity_factor);
+  if (s != MOE_OK) return s;
+  if (!out) return moe::fail(MOE_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!w || !w->w13 || !w->w13_scale || !w->w2 || !w->w2_scale)
+    return moe::fail(MOE_ERR_INVALID_ARG, "weights or a weight pointer is NULL");
+  if (((uintptr_t)w->w13 | (uintptr_t)w->w2) & 15)
+    return moe::fail(MOE_ERR_INVALID_ARG, "weight codes must be 16-byte aligned");
+  if (((uintptr_t)w->w13_scale | (uintptr_t)w->w2_scale) & 3)
+    return moe::fail(MOE_ERR_INVALID_ARG, "weight scales must be 4-byte aligned");
+  if (!workspace || ((uintptr_t)workspace & 255))
+    return moe::fail(MOE_ERR_INVALID_ARG, "workspace must be non-NULL and 256-byte aligned");
+  if (cfg->weight_format != MOE_WEIGHT_E4M3_BLOCK128)
+    return moe::fail(MOE_ERR_UNSUPPORTED, "MXFP8 weights are not built into this library version");
+  moe::Tactic t = moe::choose_tactic(*cfg, expected_m);
+  moe::Layout L = moe::compute_layout(*cfg, t, max_rows, capacity_factor);
+  if (ws_bytes < L.total)
+    return moe::fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < required %zu", ws_bytes, L.total);
+
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hip_fail("hipGetDevice");
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return hip_fail("hipDeviceGetAttribute");
+  moe_layer* l = new (std::nothrow) moe_layer();
+  if (!l) return moe::fail(MOE_ERR_INVALID_ARG, "out of host memory");
+  l->cfg = *cfg;
+  l->w = *w;
+  l->tac = t;
+  l->L = L;
+  l->ws = static_cast<uint8_t*>(workspace);
+  l->max_rows = max_rows;
+  l->expected_m = expected_m;
+  l->capacity_factor = capacity_factor;
+  l->staged_tokens = -1;
+  l->out = nullptr;
+  auto grid = [&](int which) {
+    int g = cus * moe::gemm_max_workgroups_per_cu(which, t.block_m);
+    g = (g / 8) * 8;
+    return g < 8 ? 8 : g;
+  };
+  l->grid_fc1 = grid(1);
+  l->grid_fc2 = grid(2);
+  l->prof = false;
+  memset(l->ms, 0, sizeof(l->ms));
+  memset(l->launches, 0, sizeof(l->launches));
+  *out = l;
+  return MOE_OK;
+}
+
+extern "C" moe_status_t moe_stage_inputs(moe_layer_t* l, const void* x, const float* x_scale,
+                                         const int32_t* topk_idx, const float* topk_w, int32_t num_tokens,
+                                         void* out_bf16, void* stream) {
+  moe::clear_error();
+  if (!l) return moe::fail(MOE_ERR_INVALID_ARG, "layer is NULL");
+  if (num_tokens < 0) return moe::fail(MOE_ERR_INVALID_ARG, "num_tokens %d < 0", num_tokens);
+  if (num_tokens > l->max_rows)
+    return moe::fail(MOE_ERR_CAPACITY, "num_tokens %d exceeds max_rows %d", num_tokens, l->max_rows);
+  if (num_tokens > 0) {
+    if (!x || !topk_idx || !topk_w || !out_bf16)
+      return moe::fail(MOE_ERR_INVALID_ARG, "x, topk_idx, topk_w and out must be non-NULL");
+    if (((uintptr_t)x | (uintptr_t)out_bf16) & 15)
+      return moe::fail(MOE_ERR_INVALID_ARG, "x and out must be 16-byte aligned");
+    if (((uintptr_t)topk_idx | (uintptr_t)topk_w | (uintptr_t)x_scale) & 3)
+      return moe::fail(MOE_ERR_INVALID_ARG, "topk_idx, topk_w and x_scale must be 4-byte aligned");
+  }
+  if (x_scale && l->cfg.act_format != MOE_ACT_E4M3_1X128)
+    return moe::fail(MOE_ERR_INVALID_ARG, "x_scale is only meaningful for E4M3_1X128 activations");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  moe::StageArgs a;
+  a.x = x;
+  a.x_scale = x_scale;
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  a.tokens = num_tokens;
+  a.max_rows = l->max_rows;
+  a.hidden = l->cfg.hidden;
+  a.top_k = l->cfg.top_k;
+  a.num_experts = l->cfg.num_experts;
+  a.flags = l->cfg.flags;
+  a.act_format = l->cfg.act_format;
+  a.hdr = region<uint32_t>(l, MOE_REGION_STATUS);
+  a.staged_idx = region<int32_t>(l, MOE_REGION_STAGED_IDX);
+  a.staged_w = region<float>(l, MOE_REGION_STAGED_W);
+  a.xq = region<uint8_t>(l, MOE_REGION_XQ);
+  a.xs = region<float>(l, MOE_REGION_XS);
+  const int p = prof_begin(l, MOE_KERNEL_STAGE, s);
+  if (moe::launch_stage(a, stream) != 0) return hip_fail("stage launch");
+  prof_end(l, p, s);
+  l->staged_tokens = num_tokens;
+  l->out = out_bf16;
+  return MOE_OK;
+}
+
+extern "C" moe_status_t moe_layer_forward(moe_layer_t* l, void* stream) {
+  moe::clear_error();
+  if (!l) return moe::fail(MOE_ERR_INVALID_ARG, "layer is NULL");
+  if (l->staged_tokens < 0) return moe::fail(MOE_ERR_STATE, "moe_stage_inputs has not been called");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const moe_config_t& c = l->cfg;
+  const int32_t T = l->staged_tokens;
+  const int32_t routes = T * c.top_k;
+
+  moe::CompactArgs ca;
+  ca.staged_idx = region<int32_t>(l, MOE_REGION_STAGED_IDX);
+  ca.routes = routes;
+  ca.num_experts = c.num_experts;
+  ca.row_cap = (int32_t)l->L.row_cap;
+  ca.block_m = l->tac.block_m;
+  ca.blocks = (routes + moe::kCompactChunk - 1) / moe::kCompactChunk;
+  ca.hdr = region<uint32_t>(l, MOE_REGION_STATUS);
+  ca.blk_base = region<int32_t>(l, moe::kRegionBlkBase);
+  ca.counts = region<int32_t>(l, MOE_REGION_COUNTS);
+  ca.offsets = region<int32_t>(l, MOE_REGION_OFFSETS);
+  ca.sorted_route = region<int32_t>(l, MOE_REGION_SORTED_ROUTE);
+  ca.route_pos = region<int32_t>(l, MOE_REGION_ROUTE_POS);
+  ca.tiles = region<int32_t>(l, MOE_REGION_TILES);
+  int p = prof_begin(l, MOE_KERNEL_COMPACT, s);
+  if (moe::launch_compact(ca, stream) != 0) return hip_fail("compact launch");
+  prof_end(l, p, s);
+
+  moe::GemmArgs g1;
+  memset(&g1, 0, sizeof(g1));
+  g1.a = region<uint8_t>(l, MOE_REGION_XQ);
+  g1.a_scale = region<float>(l, MOE_REGION_XS);
+  g1.a_mode = (c.flags & MOE_FLAG_PER_ROUTE_STAGING) ? 2 : 1;
+  g1.sorted_route = ca.sorted_route;
+  g1.top_k = c.top_k;
+  g1.w = static_cast<const uint8_t*>(l->w.w13);
+  g1.w_scale = static_cast<const float*>(l->w.w13_scale);
+  g1.n_rows = 2 * c.intermediate;
+  g1.k_dim = c.hidden;
+  g1.inter = c.intermediate;
+  g1.n_tiles = c.intermediate / 128;
+  g1.tiles = ca.tiles;
+  g1.offsets = ca.offsets;
+  g1.hdr = ca.hdr;
+  g1.hq = region<uint8_t>(l, MOE_REGION_HQ);
+  g1.hs = region<float>(l, MOE_REGION_HS);
+  g1.grid = l->grid_fc1;
+  p = prof_begin(l, MOE_KERNEL_FC1, s);
+  if (moe::launch_fc1(g1, l->tac.block_m, stream) != 0) return hip_fail("fc1 launch");
+  prof_end(l, p, s);
+
+  moe::GemmArgs g2;
+  memset(&g2, 0, sizeof(g2));
+  g2.a = g1.hq;
+  g2.a_scale = g1.hs;
+  g2.a_mode = 0;
+  g2.sorted_route = ca.sorted_route;
+  g2.top_k = c.top_k;
+  g2.w = static_cast<const uint8_t*>(l->w.w2);
+  g2.w_scale = static_cast<const float*>(l->w.w2_scale);
+  g2.n_rows = c.hidden;
+  g2.k_dim = c.intermediate;
+  g2.inter = c.intermediate;
+  g2.n_tiles = (c.hidden + 255) / 256;
+  g2.tiles = ca.tiles;
+  g2.offsets = ca.offsets;
+  g2.hdr = ca.hdr;
+  g2.y = region<uint16_t>(l, MOE_REGION_Y);
+  g2.grid = l->grid_fc2;
+  p = prof_begin(l, MOE_KERNEL_FC2, s);
+  if (moe::launch_fc2(g2, l->tac.block_m, stream) != 0) return hip_fail("fc2 launch");
+  prof_end(l, p, s);
+
+  moe::CombineArgs cb;
+  cb.y = g2.y;
+  cb.route_pos = ca.route_pos;
+  cb.staged_w = region<float>(l, MOE_REGION_STAGED_W);
+  cb.tokens = T;
+  cb.top_k = c.top_k;
+  cb.hidden = c.hidden;
+  cb.out = static_cast<uint16_t*>(l->out);
+  p = prof_begin(l, MOE_KERNEL_COMBINE, s);
+  if (moe::launch_combine(cb, stream) != 0) return hip_fail("combine launch");
+  prof_end(l, p, s);
+  return MOE_OK;
+}
+
+extern "C" moe_status_t moe_read_status(moe_layer_t* l, void* stream, uint32_t* bits) {
+  moe::clear_error();
+  if (!l || !bits) return moe::fail(MOE_ERR_INVALID_ARG, "layer and bits must be non-NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  if (hipMemcpyAsync(&v, region<uint32_t>(l, MOE_REGION_STATUS), sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return hip_fail("hipMemcpyAsync");
+  if (hipStreamSynchronize(s) != hipSuccess) return hip_fail("hipStreamSynchronize");
+  *bits = v;
+  return MOE_OK;
+}
+
+extern "C" moe_status_t moe_layer_region(moe_layer_t* l, int32_t r, void** dptr, size_t* bytes) {
+  moe::clear_error();
+  if (!l || !dptr || !bytes) return moe::fail(MOE_ERR_INVALID_ARG, "NULL argument");
+  if (r < 0 || r > MOE_REGION_TILES) return moe::fail(MOE_ERR_INVALID_ARG, "unknown region %d", r);
+  *dptr = l->ws + l->L.off[r];
+  *bytes = l->L.size[r];
+  return MOE_OK;
+}
+
+extern "C" moe_status_t moe_layer_tactic(const moe_layer_t* l, moe_tactic_t* t) {
+  moe::clear_error();
+  if (!l || !t) return moe::fail(MOE_ERR_INVALID_ARG, "NULL argument");
+  t->token_bucket = l->tac.bucket;
+  t->block_m = l->tac.block_m;
+  t->block_n = l->tac.block_n;
+  t->grid_fc1 = l->grid_fc1;
+  t->grid_fc2 = l->grid_fc2;
+  t->row_cap = (int32_t)l->L.row_cap;
+  t->max_m_tiles = (int32_t)l->L.max_m_tiles;
+  t->reserved = 0;
+  return MOE_OK;
+}
+
+extern "C" moe_status_t moe_profile_enable(moe_layer_t* l, int32_t enable) {
+  moe::clear_error();
+  if (!l) return moe::fail(MOE_ERR_INVALID_ARG, "layer is NULL");
+  l->prof = enable != 0;
+  memset(l->ms, 0, sizeof(l->ms));
+  memset(l->launches, 0, sizeof(l->launches));
+  return MOE_OK;
+}
+
+extern "C" moe_status_t moe_profile_read(moe_layer_t* l, double* ms_total, int64_t* launches) {
+  moe::clear_error();
+  if (!l || !ms_total || !launches) return moe::fail(MOE_ERR_INVALID_ARG, "NULL argument");
+  for (EventPair& p : l->pending) {
+    if (hipEventSynchronize(p.stop) != hipSuccess) return hip_fail("hipEventSynchronize");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, p.start, p.stop) != hipSuccess) return hip_fail("hipEventElapsedTime");
+    l->ms[p.kind] += ms;
+    l->launches[p.kind] += 1;
+    l->pool.push_back(p.start);
+    l->pool.push_back(p.stop);
+  }
+  l->pending.clear();
+  for (int k = 0; k < MOE_KERNEL_COUNT; ++k) {
+    ms_total[k] = l->ms[k];
+    launches[k] = l->launches[k];
+  }
+  return MOE_OK;
+}
+
+extern "C" moe_status_t moe_layer_destroy(moe_layer_t* l) {
+  moe::clear_error();
+  if (!l) return MOE_OK;
+  for (EventPair& p : l->pending) {
+    (void)hipEventSynchronize(p.stop);
+    (void)hipEventDestroy(p.start);
+    (void)hipEventDestroy(p.stop);
+  }
+  for (hipEvent_t e : l->pool) (void)hipEventDestroy(e);
+  delete l;
+  return MOE_OK;
+}

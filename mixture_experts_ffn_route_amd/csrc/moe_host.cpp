@@ -1,0 +1,160 @@
+// Host-side logic with no HIP dependency: argument validation, the token
+// bucket and tile tactic table, and the workspace layout.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+static thread_local char g_last_error[512];
+
+moe_status_t fail(moe_status_t s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+const char* last_error() { return g_last_error; }
+void clear_error() { g_last_error[0] = 0; }
+
+// Clamped ceil power of two in [8, 32768]: the token bucket of the SM90
+// pull-style MegaMoE heuristics (flashinfer PR #4688, heuristic-config test).
+int32_t token_bucket(int32_t tokens) {
+  if (tokens <= 0) return -1;
+  if (tokens >= 32768) return 32768;
+  int32_t b = 8;
+  while (b < tokens) b <<= 1;
+  return b;
+}
+
+static bool valid_top_k(int k) { return k == 1 || k == 2 || k == 4 || k == 6 || k == 8; }
+
+moe_status_t validate_config(const moe_config_t* cfg, int32_t expected_m, int32_t max_rows,
+                             float capacity_factor) {
+  if (!cfg) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
+  if (cfg->hidden <= 0 || cfg->intermediate <= 0)
+    return fail(MOE_ERR_INVALID_ARG, "hidden (%d) and intermediate (%d) must be positive", cfg->hidden,
+                cfg->intermediate);
+  if (cfg->hidden % 128 || cfg->intermediate % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "hidden (%d) and intermediate (%d) must be multiples of 128",
+                cfg->hidden, cfg->intermediate);
+  if (cfg->hidden > 65536 || cfg->intermediate > 65536)
+    return fail(MOE_ERR_UNSUPPORTED, "hidden/intermediate above 65536 are not supported");
+  if (cfg->num_experts < 1 || cfg->num_experts > kMaxExperts)
+    return fail(MOE_ERR_UNSUPPORTED, "num_experts %d outside [1, %d]", cfg->num_experts, kMaxExperts);
+  if (!valid_top_k(cfg->top_k))
+    return fail(MOE_ERR_UNSUPPORTED, "top_k %d not in {1, 2, 4, 6, 8}", cfg->top_k);
+  if (cfg->top_k > cfg->num_experts)
+    return fail(MOE_ERR_INVALID_ARG, "top_k %d exceeds num_experts %d", cfg->top_k, cfg->num_experts);
+  if (cfg->flags & ~(uint32_t)(MOE_FLAG_CHECK_ROUTES | MOE_FLAG_PER_ROUTE_STAGING))
+    return fail(MOE_ERR_INVALID_ARG, "unknown flag bits 0x%x", cfg->flags);
+  if (cfg->weight_format == MOE_WEIGHT_E4M3_BLOCK128) {
+    if (cfg->act_format != MOE_ACT_E4M3_1X128)
+      return fail(MOE_ERR_UNSUPPORTED, "E4M3_BLOCK128 weights need E4M3_1X128 activations");
+  } else if (cfg->weight_format == MOE_WEIGHT_MXFP8_E4M3) {
+    if (cfg->act_format != MOE_ACT_BF16)
+      return fail(MOE_ERR_UNSUPPORTED, "MXFP8 weights need BF16 activations");
+    if (cfg->flags & MOE_FLAG_PER_ROUTE_STAGING)
+      return fail(MOE_ERR_UNSUPPORTED, "per-route staging is only provided for the FP8 path");
+  } else {
+    return fail(MOE_ERR_INVALID_ARG, "unknown weight_format %d", cfg->weight_format);
+  }
+  if (expected_m < 1) return fail(MOE_ERR_INVALID_ARG, "expected_m %d must be >= 1", expected_m);
+  if (max_rows < 1) return fail(MOE_ERR_INVALID_ARG, "max_rows %d must be >= 1", max_rows);
+  if ((int64_t)max_rows * cfg->top_k > (int64_t)1 << 30)
+    return fail(MOE_ERR_UNSUPPORTED, "max_rows * top_k above 2^30");
+  if (!(capacity_factor > 0.0f) || !isfinite(capacity_factor))
+    return fail(MOE_ERR_INVALID_ARG, "capacity_factor must be finite and > 0");
+  return MOE_OK;
+}
+
+// Tile tactic from the expected rows per expert.  block_m follows the token
+// bucket; weights always come in 256-row tiles (FC1: 128 gate + 128 up rows
+// of one 128-wide output block; FC2: two 128-row blocks of H).
+Tactic choose_tactic(const moe_config_t& cfg, int32_t expected_m) {
+  (void)cfg;
+  Tactic t;
+  t.bucket = token_bucket(expected_m);
+  t.block_n = 256;
+  t.stages = 2;
+  if (t.bucket <= 32)
+    t.block_m = 32;
+  else if (t.bucket <= 64)
+    t.block_m = 64;
+  else
+    t.block_m = 128;
+  return t;
+}
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+Layout compute_layout(const moe_config_t& cfg, const Tactic& t, int32_t max_rows, float capacity_factor) {
+  Layout L;
+  memset(&L, 0, sizeof(L));
+  const int64_t K = cfg.top_k, H = cfg.hidden, I = cfg.intermediate, E = cfg.num_experts;
+  const bool bf16_act = cfg.act_format == MOE_ACT_BF16;
+  L.route_slots = (int64_t)max_rows * K;
+  L.rows_x = (cfg.flags & MOE_FLAG_PER_ROUTE_STAGING) ? L.route_slots : max_rows;
+  double cap = ceil((double)capacity_factor * (double)L.route_slots);
+  L.row_cap = cap >= (double)L.route_slots ? L.route_slots : (int64_t)cap;
+  if (L.row_cap < 1) L.row_cap = 1;
+  L.max_m_tiles = (L.row_cap + t.block_m - 1) / t.block_m + E;
+  L.compact_blocks = (L.route_slots + kCompactChunk - 1) / kCompactChunk;
+
+  L.size[MOE_REGION_STATUS] = 256;
+  L.size[MOE_REGION_STAGED_IDX] = L.route_slots * 4;
+  L.size[MOE_REGION_STAGED_W] = L.route_slots * 4;
+  L.size[MOE_REGION_XQ] = L.rows_x * H * (bf16_act ? 2 : 1);
+  L.size[MOE_REGION_XS] = bf16_act ? 0 : L.rows_x * (H / 128) * 4;
+  L.size[MOE_REGION_COUNTS] = E * 4;
+  L.size[MOE_REGION_OFFSETS] = (E + 1) * 4;
+  L.size[MOE_REGION_SORTED_ROUTE] = L.row_cap * 4;
+  L.size[MOE_REGION_ROUTE_POS] = L.route_slots * 4;
+  L.size[MOE_REGION_HQ] = L.row_cap * I * (bf16_act ? 2 : 1);
+  L.size[MOE_REGION_HS] = bf16_act ? 0 : L.row_cap * (I / 128) * 4;
+  L.size[MOE_REGION_Y] = L.row_cap * H * 2;
+  L.size[MOE_REGION_TILES] = L.max_m_tiles * 2 * 4;
+  L.size[kRegionBlkBase] = L.compact_blocks * E * 4;
+  size_t off = 0;
+  for (int r = 0; r < kNumRegions; ++r) {
+    L.off[r] = off;
+    off += align256(L.size[r]);
+  }
+  L.total = off;
+  return L;
+}
+
+}  // namespace moe
+
+extern "C" int32_t moe_token_bucket(int32_t tokens) { return moe::token_bucket(tokens); }
+
+extern "C" const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_CAPACITY: return "MOE_ERR_CAPACITY";
+    case MOE_ERR_STATE: return "MOE_ERR_STATE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+extern "C" const char* moe_last_error(void) { return moe::last_error(); }
+
+extern "C" moe_status_t moe_workspace_query(const moe_config_t* cfg, int32_t expected_m, int32_t max_rows,
+                                            float capacity_factor, size_t* ws_bytes) {
+  moe::clear_error();
+  moe_status_t s = moe::validate_config(cfg, expected_m, max_rows, capacity_factor);
+  if (s != MOE_OK) return s;
+  if (!ws_bytes) return moe::fail(MOE_ERR_INVALID_ARG, "ws_bytes is NULL");
+  moe::Tactic t = moe::choose_tactic(*cfg, expected_m);
+  *ws_bytes = moe::compute_layout(*cfg, t, max_rows, capacity_factor).total;
+  return MOE_OK;
+}

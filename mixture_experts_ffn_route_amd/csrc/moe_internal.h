@@ -1,0 +1,125 @@
+// Internal declarations shared by the host side and the kernel launchers.
+// Nothing here is part of the public ABI (include/moe.h).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kMaxExperts = 1024;
+constexpr int kCompactChunk = 4096;  // routes per compaction workgroup (256 lanes x 16)
+constexpr int kNumRegions = 14;
+constexpr int kRegionBlkBase = 13;   // internal: per-(compaction block, expert) bases
+
+// Words of the device header (MOE_REGION_STATUS).
+enum HeaderWord : int {
+  kHdrStatus = 0,      // MOE_DEV_* bits
+  kHdrTokens = 1,      // tokens staged
+  kHdrRoutes = 2,      // routes kept after compaction (R)
+  kHdrMTiles = 3,      // (expert, row-tile) pairs in the tile list
+};
+
+struct Tactic {
+  int32_t bucket;
+  int32_t block_m;
+  int32_t block_n;
+  int32_t stages;
+};
+
+struct Layout {
+  int64_t rows_x;       // staged activation rows (max_rows, or max_rows*K per-route)
+  int64_t route_slots;  // max_rows * K
+  int64_t row_cap;      // route rows held by h/y
+  int64_t max_m_tiles;  // bound on the tile list length
+  int64_t compact_blocks;
+  size_t off[kNumRegions];
+  size_t size[kNumRegions];
+  size_t total;
+};
+
+// Host-only logic (moe_host.cpp, no HIP dependency).
+int32_t token_bucket(int32_t tokens);
+moe_status_t validate_config(const moe_config_t* cfg, int32_t expected_m, int32_t max_rows,
+                             float capacity_factor);
+Tactic choose_tactic(const moe_config_t& cfg, int32_t expected_m);
+Layout compute_layout(const moe_config_t& cfg, const Tactic& t, int32_t max_rows, float capacity_factor);
+moe_status_t fail(moe_status_t s, const char* fmt, ...);
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (moe_*.hip).  All take a hipStream_t as void*.
+// ---------------------------------------------------------------------------
+
+struct StageArgs {
+  const void* x;          // bf16 [T, H] or e4m3 [T, H]
+  const float* x_scale;   // null for bf16 input
+  const int32_t* topk_idx;
+  const float* topk_w;
+  int32_t tokens, max_rows, hidden, top_k, num_experts;
+  uint32_t flags;
+  int32_t act_format;
+  // workspace
+  uint32_t* hdr;
+  int32_t* staged_idx;
+  float* staged_w;
+  uint8_t* xq;            // e4m3 rows (or bf16 rows for the MX variant)
+  float* xs;
+};
+int launch_stage(const StageArgs& a, void* stream);
+
+struct CompactArgs {
+  const int32_t* staged_idx;
+  int32_t routes;          // T*K
+  int32_t num_experts;
+  int32_t row_cap;
+  int32_t block_m;
+  int32_t blocks;          // compaction workgroups
+  uint32_t* hdr;
+  int32_t* blk_base;       // [blocks, E]
+  int32_t* counts;         // [E]
+  int32_t* offsets;        // [E+1]
+  int32_t* sorted_route;   // [row_cap]
+  int32_t* route_pos;      // [routes]
+  int32_t* tiles;          // [max_m_tiles, 2]
+};
+int launch_compact(const CompactArgs& a, void* stream);
+
+struct GemmArgs {
+  // A operand: activation rows
+  const uint8_t* a;        // e4m3 rows
+  const float* a_scale;    // [rows, K/128]
+  int32_t a_mode;          // 0: sorted position p; 1: token = route/K; 2: route id
+  const int32_t* sorted_route;
+  int32_t top_k;
+  // B operand: expert weights [E, N, K]
+  const uint8_t* w;
+  const float* w_scale;    // [E, N/128, K/128]
+  int32_t n_rows;          // N (2I for FC1, H for FC2)
+  int32_t k_dim;           // K (H for FC1, I for FC2)
+  int32_t inter;           // I (FC1 gate/up split)
+  int32_t n_tiles;         // output column tiles
+  // tiles
+  const int32_t* tiles;    // (expert, first sorted row)
+  const int32_t* offsets;  // kept offsets [E+1]
+  const uint32_t* hdr;
+  // outputs
+  uint8_t* hq;  float* hs; // FC1: e4m3 [R, I], scales [R, I/128]
+  uint16_t* y;             // FC2: bf16 [R, H]
+  int32_t grid;
+};
+int launch_fc1(const GemmArgs& a, int block_m, void* stream);
+int launch_fc2(const GemmArgs& a, int block_m, void* stream);
+int gemm_max_workgroups_per_cu(int which, int block_m);
+
+struct CombineArgs {
+  const uint16_t* y;
+  const int32_t* route_pos;
+  const float* staged_w;
+  int32_t tokens, top_k, hidden;
+  uint16_t* out;
+};
+int launch_combine(const CombineArgs& a, void* stream);
+
+}  // namespace moe

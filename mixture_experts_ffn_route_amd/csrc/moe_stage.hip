@@ -1,0 +1,130 @@
+// Forward preparation: activation quantisation to e4m3 with 1x128 scales and
+// route staging with the routing checker, after "perf(moe_ep): fuse Rubin
+// MegaMoE forward preparation" (flashinfer PR #6398: fused input quantisation
+// + route staging; checker for expert-id bounds, duplicate routes and finite
+// scores; masked slots may carry NaN/inf and are staged as zero without
+// touching the caller's tensors).
+#include <hip/hip_runtime.h>
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+// One 16-lane group per 1x128 block; each lane owns 8 consecutive columns.
+//   s = amax / 448 (IEEE float division), q = RNE_sat(x / s), s == 0 -> q = 0.
+// With a prequantised input (x_scale != null) codes and scales are copied.
+// Block 0 also resets the device header for this batch.
+__global__ __launch_bounds__(256) void stage_quant_kernel(StageArgs a, int64_t groups, int copies) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (blockIdx.x == 0 && threadIdx.x < 64) a.hdr[threadIdx.x] = threadIdx.x == kHdrTokens ? (uint32_t)a.tokens : 0u;
+  const int64_t grp = g >> 4;
+  if (grp >= groups) return;
+  const int lane16 = threadIdx.x & 15;
+  const int kbs = a.hidden >> 7;
+  const int64_t row = grp / kbs;
+  const int kb = (int)(grp - row * kbs);
+  const int64_t col = (int64_t)kb * 128 + lane16 * 8;
+  uint2 codes;
+  float s;
+  if (a.x_scale == nullptr) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + row * a.hidden + col);
+    float v[8];
+    v[0] = bf16_to_f32(raw.x & 0xffffu); v[1] = bf16_to_f32(raw.x >> 16);
+    v[2] = bf16_to_f32(raw.y & 0xffffu); v[3] = bf16_to_f32(raw.y >> 16);
+    v[4] = bf16_to_f32(raw.z & 0xffffu); v[5] = bf16_to_f32(raw.z >> 16);
+    v[6] = bf16_to_f32(raw.w & 0xffffu); v[7] = bf16_to_f32(raw.w >> 16);
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    m = group_max<16>(m);
+    s = m / kE4m3Max;
+    if (s == 0.0f) {
+      codes = make_uint2(0u, 0u);
+    } else {
+      float q[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = v[i] / s;
+      int w0 = cvt2_e4m3(q[0], q[1], 0, false);
+      w0 = cvt2_e4m3(q[2], q[3], w0, true);
+      int w1 = cvt2_e4m3(q[4], q[5], 0, false);
+      w1 = cvt2_e4m3(q[6], q[7], w1, true);
+      codes = make_uint2((uint32_t)w0, (uint32_t)w1);
+    }
+  } else {
+    codes = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(a.x) + row * a.hidden + col);
+    s = a.x_scale[row * kbs + kb];
+  }
+  for (int c = 0; c < copies; ++c) {
+    const int64_t dst = row * copies + c;
+    *reinterpret_cast<uint2*>(a.xq + dst * a.hidden + col) = codes;
+    if (lane16 == 0) a.xs[dst * kbs + kb] = s;
+  }
+}
+
+// One thread per token slot row in [0, max_rows).  Live rows are checked and
+// masked; rows past the live count are staged as masked.
+__global__ __launch_bounds__(256) void stage_routes_kernel(StageArgs a) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= a.max_rows) return;
+  const int K = a.top_k;
+  uint32_t bits = 0;
+  int ids[8];
+  float ws[8];
+  bool act[8];
+  for (int k = 0; k < K; ++k) {
+    ids[k] = -1;
+    ws[k] = 0.0f;
+    act[k] = false;
+  }
+  if (t < a.tokens) {
+    for (int k = 0; k < K; ++k) {
+      const int e = a.topk_idx[(int64_t)t * K + k];
+      const float w = a.topk_w[(int64_t)t * K + k];
+      ids[k] = e;
+      ws[k] = w;
+      if (e == -1) continue;
+      if (e < -1 || e >= a.num_experts) {
+        bits |= MOE_DEV_BAD_EXPERT;
+        continue;
+      }
+      act[k] = true;
+    }
+    if (a.flags & MOE_FLAG_CHECK_ROUTES) {
+      for (int k = 1; k < K; ++k) {
+        if (!act[k]) continue;
+        for (int j = 0; j < k; ++j) {
+          if (act[j] && ids[j] == ids[k]) {  // the lowest slot of an id stays active
+            act[k] = false;
+            bits |= MOE_DEV_DUPLICATE;
+            break;
+          }
+        }
+      }
+      for (int k = 0; k < K; ++k) {
+        if (act[k] && !isfinite(ws[k])) {
+          act[k] = false;
+          bits |= MOE_DEV_NONFINITE;
+        }
+      }
+    }
+  }
+  for (int k = 0; k < K; ++k) {
+    a.staged_idx[(int64_t)t * K + k] = act[k] ? ids[k] : -1;
+    a.staged_w[(int64_t)t * K + k] = act[k] ? ws[k] : 0.0f;
+  }
+  if (bits) atomicOr(a.hdr + kHdrStatus, bits);
+}
+
+int launch_stage(const StageArgs& a, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t groups = (int64_t)a.tokens * (a.hidden / 128);
+  const int64_t threads = groups * 16;
+  const int qblocks = (int)((threads + 255) / 256);
+  const int copies = (a.flags & MOE_FLAG_PER_ROUTE_STAGING) ? a.top_k : 1;
+  hipLaunchKernelGGL(stage_quant_kernel, dim3(qblocks > 0 ? qblocks : 1), dim3(256), 0, s, a, groups, copies);
+  hipLaunchKernelGGL(stage_routes_kernel, dim3((a.max_rows + 255) / 256), dim3(256), 0, s, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace moe

@@ -1,0 +1,136 @@
+"""Host-side checks of the C-ABI library (no GPU): it loads, exports every
+symbol include/moe.h declares, and its synchronous validation returns the
+documented errors before anything is launched."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_ffn_route_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    with open(os.path.join(ROOT, "include", "moe.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:[A-Za-z_][\w\s\*]*?)\b(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _header_functions()
+    assert len(names) >= 13
+    assert sorted(names) == sorted(L.EXPORTS)
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_token_bucket_matches_pages_table():
+    path = os.path.join(ROOT, "tests", "golden", "token_bucket.txt")
+    rows = [ln.split() for ln in open(path) if ln.strip() and not ln.startswith("#")]
+    assert rows
+    for tokens, bucket in rows:
+        got = L.moe_token_bucket(int(tokens))
+        if bucket == "error":
+            assert got < 0
+        else:
+            assert got == int(bucket), (tokens, bucket, got)
+
+
+def _cfg(**kw):
+    base = dict(hidden=7168, intermediate=2048, num_experts=32, top_k=8)
+    base.update(kw)
+    return L.make_config(base["hidden"], base["intermediate"], base["num_experts"], base["top_k"],
+                         kw.get("weight_format", L.MOE_WEIGHT_E4M3_BLOCK128),
+                         kw.get("act_format", L.MOE_ACT_E4M3_1X128), kw.get("flags", L.MOE_FLAG_CHECK_ROUTES))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(top_k=3), L.MOE_ERR_UNSUPPORTED),
+    (dict(top_k=10), L.MOE_ERR_UNSUPPORTED),
+    (dict(hidden=7000), L.MOE_ERR_UNSUPPORTED),
+    (dict(intermediate=100), L.MOE_ERR_UNSUPPORTED),
+    (dict(hidden=0), L.MOE_ERR_INVALID_ARG),
+    (dict(num_experts=0), L.MOE_ERR_UNSUPPORTED),
+    (dict(num_experts=2000), L.MOE_ERR_UNSUPPORTED),
+    (dict(num_experts=4, top_k=6), L.MOE_ERR_INVALID_ARG),
+    (dict(flags=0x80), L.MOE_ERR_INVALID_ARG),
+    (dict(act_format=L.MOE_ACT_BF16), L.MOE_ERR_UNSUPPORTED),
+    (dict(weight_format=L.MOE_WEIGHT_MXFP8_E4M3), L.MOE_ERR_UNSUPPORTED),
+    (dict(weight_format=7), L.MOE_ERR_INVALID_ARG),
+])
+def test_query_rejects_bad_config(kw, status):
+    with pytest.raises(L.MoEError) as ei:
+        L.moe_workspace_query(_cfg(**kw), 64, 128, 1.0)
+    assert ei.value.status == status
+    assert L.moe_last_error()
+
+
+@pytest.mark.parametrize("expected_m,max_rows,cf,status", [
+    (0, 128, 1.0, L.MOE_ERR_INVALID_ARG),
+    (64, 0, 1.0, L.MOE_ERR_INVALID_ARG),
+    (64, 128, 0.0, L.MOE_ERR_INVALID_ARG),
+    (64, 128, float("nan"), L.MOE_ERR_INVALID_ARG),
+    (64, 128, float("inf"), L.MOE_ERR_INVALID_ARG),
+    (64, 1 << 28, 1.0, L.MOE_ERR_UNSUPPORTED),
+])
+def test_query_rejects_bad_sizes(expected_m, max_rows, cf, status):
+    with pytest.raises(L.MoEError) as ei:
+        L.moe_workspace_query(_cfg(), expected_m, max_rows, cf)
+    assert ei.value.status == status
+
+
+def test_query_sizes_scale_with_capacity_not_tactic():
+    cfg = _cfg()
+    a = L.moe_workspace_query(cfg, 8, 4096, 1.0)
+    b = L.moe_workspace_query(cfg, 8, 8192, 1.0)
+    c = L.moe_workspace_query(cfg, 8, 4096, 0.5)
+    assert a % 256 == 0 and b > a and c < a
+    # the y buffer dominates: row_cap * H * 2 bytes
+    assert a >= 4096 * 8 * 7168 * 2
+    # tactic (expected_m) changes only the tile list bound
+    d = L.moe_workspace_query(cfg, 4096, 4096, 1.0)
+    assert abs(d - a) < 64 * 1024
+    e = L.moe_workspace_query(_cfg(flags=L.MOE_FLAG_CHECK_ROUTES | L.MOE_FLAG_PER_ROUTE_STAGING), 8, 4096, 1.0)
+    assert e - a >= 4096 * 7 * 7168  # K copies of each activation row
+
+
+def test_create_validation_before_any_launch():
+    cfg = _cfg(hidden=256, intermediate=128, num_experts=8, top_k=2)
+    n = L.moe_workspace_query(cfg, 4, 16, 1.0)
+    # NULL weights
+    with pytest.raises(L.MoEError) as ei:
+        L.moe_layer_create(cfg, 4, 16, 1.0, 0, 0, 0, 0, 4096, n)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARG
+    # misaligned weight codes
+    with pytest.raises(L.MoEError) as ei:
+        L.moe_layer_create(cfg, 4, 16, 1.0, 4097, 4096, 4096, 4096, 4096, n)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARG
+    # misaligned workspace
+    with pytest.raises(L.MoEError) as ei:
+        L.moe_layer_create(cfg, 4, 16, 1.0, 4096, 4096, 4096, 4096, 4096 + 16, n)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARG
+    # workspace too small
+    with pytest.raises(L.MoEError) as ei:
+        L.moe_layer_create(cfg, 4, 16, 1.0, 4096, 4096, 4096, 4096, 4096, n - 256)
+    assert ei.value.status == L.MOE_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_null_handle_calls_fail_cleanly():
+    for fn, args in [(L.moe_layer_forward, (0, 0)), (L.moe_read_status, (0, 0)), (L.moe_layer_tactic, (0,)),
+                     (L.moe_profile_enable, (0, True)), (L.moe_profile_read, (0,)), (L.moe_layer_region, (0, 0))]:
+        with pytest.raises(L.MoEError) as ei:
+            fn(*args)
+        assert ei.value.status == L.MOE_ERR_INVALID_ARG
+    with pytest.raises(L.MoEError):
+        L.moe_stage_inputs(0, 0, 0, 0, 0, 1, 0, 0)
+    L.moe_layer_destroy(0)  # no-op
+
+
+def test_status_strings():
+    for s in range(0, -7, -1):
+        assert L.status_string(s).startswith("MOE_")
+    assert L.status_string(-99) == "MOE_ERR_UNKNOWN"
