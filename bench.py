@@ -84,7 +84,9 @@ def main():
     ap.add_argument("--config", default="dsv3", choices=["tiny", "small", "dsv3", "skewed"])
     ap.add_argument("--tokens", type=int, default=None, help="override T (token sweep)")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-sample", type=int, default=384, help="tokens for the CPU oracle baseline (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens for the CPU oracle baseline (0: skip)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run one device-to-device copy of this many MiB (reference for HBM byte counters)")
     ap.add_argument("--sweep", default="", help="comma-separated token counts; extra lines to --sweep-out")
     ap.add_argument("--sweep-out", default="gpurun_out/sweep.jsonl")
     args = ap.parse_args()
@@ -148,6 +150,16 @@ def main():
         layer.close()
         del layer
         torch.cuda.empty_cache()
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {n} bytes done")
+        del src, dst
 
     T = args.tokens or base.tokens
     shape, inp, layer, sec, prof, status, counts = measure(T, args.steps, args.warmup)

@@ -89,8 +89,8 @@ enum {
 };
 
 typedef struct {
-  int32_t hidden;         /* H, multiple of 128 */
-  int32_t intermediate;   /* I, multiple of 128 (FC1 produces 2I: gate rows then up rows) */
+  int32_t hidden;         /* H, multiple of 128, <= 16384 */
+  int32_t intermediate;   /* I, multiple of 128, <= 16384 (FC1 produces 2I: gate rows then up rows) */
   int32_t num_experts;    /* E local experts, 1..1024 */
   int32_t top_k;          /* K in {1, 2, 4, 6, 8} (Limitations of PR #4069) */
   int32_t weight_format;  /* MOE_WEIGHT_* */

@@ -13,22 +13,27 @@
 //
 // Design (CDNA4):
 //  * One K-block of 128 is exactly one v_mfma_f32_16x16x128_f8f6f4.  Its FP32
-//    result is promoted into the accumulator with the product of the row's
-//    activation scale and the weight block's scale (one FMA per output per
-//    K-block), so no FP8 operand is ever rescaled.
-//  * Workgroup tile: BM rows x 256 weight rows, 4 waves as 2 (rows) x 2
-//    (columns).  FC1's 256 weight rows are the gate and up rows of one
-//    128-wide block of h, so the SwiGLU and the 1x128 amax of the epilogue see
-//    whole blocks.  FC2's are two 128-row blocks of H.
-//  * K-blocks are staged global -> registers -> LDS, double buffered, with
-//    16-byte chunks XOR-swizzled by row so MFMA operand reads are conflict
-//    free.  FC1 gathers its activation rows by token (one staged row per
-//    token: deduplicated staging).
-//  * Persistent workgroups: the (row tile, column tile) space is split into
-//    eight contiguous ranges, one per XCD (workgroup i runs on XCD i % 8), and
-//    neighbouring tiles on an XCD share activation rows and weight columns in
-//    its L2.
+//    result is promoted into an accumulator held in architectural VGPRs with
+//    one FMA by sx[token] * s_w[block] per output per K-block.
+//  * Weights are the MFMA row operand and tokens the column operand, so a
+//    lane's four outputs of a 16x16 block share one token and one weight
+//    block: one scale product per lane per token block.
+//  * Workgroup tile: 256 weight rows x BT tokens, 8 waves (two per SIMD, so
+//    one wave's promotion FMAs run beside the other's MFMAs).  FC1's 256
+//    weight rows are the gate and up rows of one 128-wide block of h, so the
+//    SwiGLU and the 1x128 amax of the epilogue see whole blocks; FC2's are
+//    two 128-row blocks of H.
+//  * K-blocks move global -> LDS by LDS-DMA (global_load_lds_dwordx4), a
+//    multi-stage ring, no staging registers.  The source address of each
+//    lane is chosen so the 16-byte chunks land XOR-swizzled by row, which
+//    keeps the MFMA operand reads free of bank conflicts.  FC1 gathers its
+//    token rows through the sorted route list (one staged row per token).
+//  * Persistent workgroups: the (token tile, column tile) space is split into
+//    eight contiguous ranges, one per XCD (workgroup i runs on XCD i % 8), so
+//    neighbouring tiles on an XCD share rows and weights in its L2.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "moe_device.h"
 #include "moe_internal.h"
@@ -38,59 +43,123 @@ namespace moe {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
-constexpr int kBN = 256;         // weight rows per tile
-constexpr int kKB = 128;         // bytes (= e4m3 elements) per K-block
-constexpr int kGroupM = 4;       // row tiles per XCD-local group
+constexpr int kThreads = 512;
+constexpr int kWaves = 8;
+constexpr int kBN = 256;          // weight rows per tile
+constexpr int kKB = 128;          // bytes (= e4m3 elements) per K-block
+constexpr int kGroupM = 4;        // token tiles per XCD-local group
+constexpr int kLdsBytes = 160 * 1024;
+constexpr int kMaxKBlocks = 128;  // K <= 16384
+constexpr int kWsBytes = 2 * kMaxKBlocks * 4;  // per-tile weight-scale columns
+constexpr int kRingBytes = kLdsBytes - kWsBytes;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kKB + ((chunk ^ (row & 7)) << 4); }
+// Physical 16-byte chunk of logical chunk c in row r.  Rows r..r+7 and the
+// even/odd rows of r..r+15 all land on distinct chunk positions.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r & 1) << 2) ^ ((r >> 1) & 7)); }
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b) {
   const v4f z = {0.f, 0.f, 0.f, 0.f};
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
 }
 
+// The 32 K-bytes lane l contributes to a 16x16x128 MFMA: row (l % 16),
+// logical chunks 2*(l/16) and 2*(l/16)+1.
 __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int row, int c0) {
-  const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + swz(row, c0));
-  const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + swz(row, c0 + 1));
+  const uint8_t* base = tile + row * kKB;
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(base + (swz(row, c0) << 4));
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(base + (swz(row, c0 + 1) << 4));
   v8i r;
   r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];
   r[4] = (int)hi[0]; r[5] = (int)hi[1]; r[6] = (int)hi[2]; r[7] = (int)hi[3];
   return r;
 }
 
-template <int BM, bool FC1>
-struct GemmTile {
-  static constexpr int WM = BM / 2;          // rows per wave
-  static constexpr int RB = WM / 16;         // 16-row MFMA blocks per wave
-  static constexpr int CB = 8;               // 16-col MFMA blocks per wave (4 per 128-block)
-  static constexpr int A_CHUNKS = BM * 8 / kThreads;   // 16-byte A chunks per thread per K-block
-  static constexpr int B_CHUNKS = kBN * 8 / kThreads;  // 8
-  static constexpr int A_BYTES = BM * kKB;
-  static constexpr int B_BYTES = kBN * kKB;
-  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + BM * 4;
-  static constexpr int OUT_BYTES = FC1 ? (BM * 128 + BM * 4 * 3) : (BM * kBN * 2);
-  static constexpr int LDS_BYTES = (2 * STAGE_BYTES > OUT_BYTES) ? 2 * STAGE_BYTES : OUT_BYTES;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// LDS-DMA (global_load_lds): lane L's bytes land at lds_wave_base + L * size;
+// lds_wave_base is wave-uniform and goes through M0.  Issued as inline asm so
+// the compiler's wait insertion, which cannot follow which ring stage a DMA
+// fills across the loop back-edge, never drains the ring; the K loop waits
+// on the vector-memory counter itself.  The "memory" clobber keeps every LDS
+// access in program order around these instructions.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)p);
+}
+__device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const float* src, uint8_t* lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// Workgroup barrier without a memory fence (no implied wait on the ring).
+__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int BT>
+struct Cfg {
+  static constexpr int WN = BT >= 64 ? 2 : (BT == 32 ? 4 : 8);  // waves along weight rows
+  static constexpr int WT = kWaves / WN;                          // waves along tokens
+  static constexpr int G = 128 / WN;                              // rows of each 128-row block per wave
+  static constexpr int NB = 2 * G / 16;                           // 16-row weight blocks per wave
+  static constexpr int TW = BT / WT;                              // tokens per wave
+  static constexpr int TBW = TW / 16;                             // 16-token blocks per wave
+  static constexpr int A_BYTES = kBN * kKB;
+  static constexpr int B_BYTES = BT * kKB;
+  static constexpr int S_BYTES = ((BT * 4 + 255) / 256) * 256;
+  static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+  static constexpr int STAGES = (kRingBytes / STAGE) > 4 ? 4 : (kRingBytes / STAGE);
+  static constexpr int A_INSTR = A_BYTES / 1024 / kWaves;         // 4
+  static constexpr int B_INSTR = (BT + 63) / 64;                  // token-chunk loads per wave
+  static constexpr int B_LANES = BT < 64 ? BT : 64;
+  static constexpr int S_LANES = BT / kWaves;                     // scale loads per wave
+  static constexpr int N_LD = A_INSTR + B_INSTR + 1;              // vector loads per wave per stage
+  static_assert(TBW >= 1 && NB >= 2 && STAGES >= 2, "tile shape");
+  static_assert((STAGES - 2) * N_LD < 64, "vmcnt range");
 };
 
-template <int BM, bool FC1>
+template <int BT, bool FC1>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
-  using G = GemmTile<BM, FC1>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS_BYTES];
+  using C = Cfg<BT>;
+  // One LDS object per ring stage: the compiler tracks LDS-DMA per object,
+  // so reading one stage never waits for the DMA still filling another.
+  __shared__ __attribute__((aligned(1024))) uint8_t ring0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring2[C::STAGES > 2 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring3[C::STAGES > 3 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) float wsc[2 * kMaxKBlocks];  // [block 0 | block 1][kb]
+  auto ring = [&](auto stage) -> uint8_t* {
+    constexpr int S = decltype(stage)::value;
+    if constexpr (S == 0) return ring0;
+    else if constexpr (S == 1) return ring1;
+    else if constexpr (S == 2) return ring2;
+    else return ring3;
+  };
+  uint8_t* smem = ring0;  // epilogue scratch
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int kbs = a.k_dim / kKB;                 // K-blocks
-  const int nblk_w = a.n_rows / 128;             // 128-row weight blocks per expert
-  const int total_m = (int)a.hdr[kHdrMTiles];
+  const int wn = wave % C::WN, wt = wave / C::WN;
+  const int kbs = a.k_dim / kKB;
+  const int nblk_w = a.n_rows / 128;
+  const int total_m = __builtin_amdgcn_readfirstlane((int)a.hdr[kHdrMTiles]);
   const int64_t total = (int64_t)total_m * a.n_tiles;
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
   const int per_xcd = gridDim.x >> 3;
   const int64_t v_begin = total * xcd / 8, v_end = total * (xcd + 1) / 8;
+  const int c0 = (lane >> 4) * 2;
 
   for (int64_t v = v_begin + slot; v < v_end; v += per_xcd) {
     // ---- tile coordinates ------------------------------------------------
@@ -100,206 +169,203 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
     const int gm = min(kGroupM, total_m - m0);
     const int nt = (int)(rem / gm);
     const int mt = m0 + (int)(rem % gm);
-    const int e = a.tiles[2 * mt];
-    const int p0 = a.tiles[2 * mt + 1];
-    const int rows_valid = min(BM, a.offsets[e + 1] - p0);
-
-    // weight blocks of this column tile
+    // tile scalars are wave-uniform; saying so keeps their dependents
+    // (weight-scale addresses) on the scalar unit
+    const int e = __builtin_amdgcn_readfirstlane(a.tiles[2 * mt]);
+    const int p0 = __builtin_amdgcn_readfirstlane(a.tiles[2 * mt + 1]);
+    const int rows_valid = min(BT, __builtin_amdgcn_readfirstlane(a.offsets[e + 1]) - p0);
     int nb0, nb1;
     if (FC1) {
-      nb0 = nt;                       // gate block
-      nb1 = a.inter / 128 + nt;       // up block
+      nb0 = nt;                  // gate block
+      nb1 = a.inter / 128 + nt;  // up block
     } else {
       nb0 = 2 * nt;
       nb1 = min(2 * nt + 1, nblk_w - 1);
     }
 
-    // ---- per-thread source addresses ------------------------------------
-    const uint8_t* a_src[G::A_CHUNKS];
+    // ---- per-lane DMA sources -------------------------------------------
+    const uint8_t* a_src[C::A_INSTR];
 #pragma unroll
-    for (int i = 0; i < G::A_CHUNKS; ++i) {
-      const int q = tid + i * kThreads;
-      const int row = q >> 3, c = q & 7;
-      const int p = p0 + min(row, rows_valid - 1);
-      int64_t src = p;
-      if (a.a_mode == 1) src = a.sorted_route[p] / a.top_k;
-      else if (a.a_mode == 2) src = a.sorted_route[p];
-      a_src[i] = a.a + src * a.k_dim + c * 16;
+    for (int j = 0; j < C::A_INSTR; ++j) {
+      const int q = wave * (C::A_INSTR * 64) + j * 64 + lane;
+      const int row = q >> 3;
+      const int wrow = (row < 128 ? nb0 * 128 + row : nb1 * 128 + row - 128);
+      a_src[j] = a.w + ((int64_t)e * a.n_rows + wrow) * a.k_dim + (swz(row, q & 7) << 4);
     }
-    const float* s_src = nullptr;
-    if (tid < BM) {
-      const int p = p0 + min(tid, rows_valid - 1);
-      int64_t src = p;
-      if (a.a_mode == 1) src = a.sorted_route[p] / a.top_k;
-      else if (a.a_mode == 2) src = a.sorted_route[p];
-      s_src = a.a_scale + src * kbs;
+    auto src_row = [&](int t) -> int64_t {
+      const int p = p0 + min(t, rows_valid - 1);
+      if (!FC1) return p;
+      const int r = a.sorted_route[p];
+      return a.a_mode == 2 ? r : r / a.top_k;
+    };
+    const uint8_t* b_src[C::B_INSTR];
+#pragma unroll
+    for (int j = 0; j < C::B_INSTR; ++j) {
+      const int q = wave * BT + j * 64 + (lane < C::B_LANES ? lane : 0);
+      const int row = q >> 3;
+      b_src[j] = a.a + src_row(row) * a.k_dim + (swz(row, q & 7) << 4);
     }
-    const uint8_t* b_src[G::B_CHUNKS];
-#pragma unroll
-    for (int i = 0; i < G::B_CHUNKS; ++i) {
-      const int q = tid + i * kThreads;
-      const int brow = q >> 3, c = q & 7;
-      const int blk = brow < 128 ? nb0 : nb1;
-      const int wrow = blk * 128 + (brow & 127);
-      b_src[i] = a.w + ((int64_t)e * a.n_rows + wrow) * a.k_dim + c * 16;
+    const float* s_src = a.a_scale + src_row(wave * C::S_LANES + (lane < C::S_LANES ? lane : 0)) * kbs;
+    // this tile's two weight-scale columns, DMA'd once per tile (waves 0-3)
+    if (wave < 4) {
+      const int blk = wave >> 1, half = wave & 1;
+      const int kb = half * 64 + lane;
+      if (kb < kbs)
+        dma4(a.w_scale + ((int64_t)e * nblk_w + (blk ? nb1 : nb0)) * kbs + kb,
+             reinterpret_cast<uint8_t*>(wsc) + (blk * kMaxKBlocks + half * 64) * 4);
     }
-    const float* ws0 = a.w_scale + ((int64_t)e * nblk_w + nb0) * kbs;
-    const float* ws1 = a.w_scale + ((int64_t)e * nblk_w + nb1) * kbs;
 
-    // ---- main loop --------------------------------------------------------
-    v4f acc[G::RB][G::CB];
+    auto issue = [&](auto stage, int kb) {
+      uint8_t* As = ring(stage);
+      uint8_t* Bs = As + C::A_BYTES;
+      uint8_t* Ss = Bs + C::B_BYTES;
 #pragma unroll
-    for (int rb = 0; rb < G::RB; ++rb)
+      for (int j = 0; j < C::A_INSTR; ++j)
+        dma16(a_src[j] + kb * kKB, As + (wave * (C::A_INSTR * 64) + j * 64) * 16);
 #pragma unroll
-      for (int cb = 0; cb < G::CB; ++cb) acc[rb][cb] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < C::B_INSTR; ++j)
+        if (lane < C::B_LANES) dma16(b_src[j] + kb * kKB, Bs + (wave * BT + j * 64) * 16);
+      if (lane < C::S_LANES) dma4(s_src + kb, Ss + wave * C::S_LANES * 4);
+    };
 
-    u32x4 ra[G::A_CHUNKS], rb_[G::B_CHUNKS];
-    float rsx = 0.f;
-#define MOE_GLOAD(KB)                                                                        \
-  do {                                                                                       \
-    _Pragma("unroll") for (int i = 0; i < G::A_CHUNKS; ++i)                                  \
-        ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + (KB) * kKB);                      \
-    _Pragma("unroll") for (int i = 0; i < G::B_CHUNKS; ++i)                                  \
-        rb_[i] = *reinterpret_cast<const u32x4*>(b_src[i] + (KB) * kKB);                     \
-    if (tid < BM) rsx = s_src[(KB)];                                                         \
-  } while (0)
-#define MOE_LSTORE(STAGE)                                                                    \
-  do {                                                                                       \
-    uint8_t* As_ = smem + (STAGE) * G::STAGE_BYTES;                                          \
-    uint8_t* Bs_ = As_ + G::A_BYTES;                                                         \
-    float* Ss_ = reinterpret_cast<float*>(Bs_ + G::B_BYTES);                                 \
-    _Pragma("unroll") for (int i = 0; i < G::A_CHUNKS; ++i) {                                \
-      const int q = tid + i * kThreads;                                                      \
-      *reinterpret_cast<u32x4*>(As_ + swz(q >> 3, q & 7)) = ra[i];                           \
-    }                                                                                        \
-    _Pragma("unroll") for (int i = 0; i < G::B_CHUNKS; ++i) {                                \
-      const int q = tid + i * kThreads;                                                      \
-      *reinterpret_cast<u32x4*>(Bs_ + swz(q >> 3, q & 7)) = rb_[i];                          \
-    }                                                                                        \
-    if (tid < BM) Ss_[tid] = rsx;                                                            \
-  } while (0)
+    v4f acc[C::NB][C::TBW];
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int tb = 0; tb < C::TBW; ++tb) acc[nb][tb] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    MOE_GLOAD(0);
-    MOE_LSTORE(0);
-    __syncthreads();
-    const int c0 = (lane >> 4) * 2;
-    for (int kb = 0; kb < kbs; ++kb) {
-      const int st = kb & 1;
-      const float sw0 = ws0[kb], sw1 = ws1[kb];
-      if (kb + 1 < kbs) MOE_GLOAD(kb + 1);
-      const uint8_t* As = smem + st * G::STAGE_BYTES;
-      const uint8_t* Bs = As + G::A_BYTES;
-      const float* Ss = reinterpret_cast<const float*>(Bs + G::B_BYTES);
-      v8i af[G::RB];
-      float sxa[G::RB][4], sxb[G::RB][4];
+    // ---- K loop: STAGES-deep LDS ring -------------------------------------
+    auto step = [&](auto stage, int kb) {
+      constexpr int ST = decltype(stage)::value;
+      const int ahead = min(C::STAGES - 2, kbs - 1 - kb);  // stages issued after this one
+      if (C::STAGES >= 4 && ahead >= 2) wait_vmcnt<(C::STAGES >= 4 ? 2 : 0) * C::N_LD>();
+      else if (C::STAGES >= 3 && ahead >= 1) wait_vmcnt<(C::STAGES >= 3 ? 1 : 0) * C::N_LD>();
+      else wait_vmcnt<0>();
+      // Every wave has its own DMA for this stage complete; the barrier makes
+      // that true for all waves.  It also orders the previous stage's LDS
+      // reads (consumed by MFMAs already) before the DMA issued next into it.
+      // A plain s_barrier: a fenced barrier would also drain the DMA of the
+      // stages still in flight.
+      barrier_nofence();
+      if (kb + C::STAGES - 1 < kbs)
+        issue(std::integral_constant<int, (ST + C::STAGES - 1) % C::STAGES>{}, kb + C::STAGES - 1);
+
+      const uint8_t* As = ring(stage);
+      const uint8_t* Bs = As + C::A_BYTES;
+      const float* Ss = reinterpret_cast<const float*>(Bs + C::B_BYTES);
+      const float sw0 = wsc[kb], sw1 = wsc[kMaxKBlocks + kb];
+      v8i bq[C::TBW];
+      float f0[C::TBW], f1[C::TBW];
 #pragma unroll
-      for (int rb = 0; rb < G::RB; ++rb) {
-        af[rb] = lds_frag(As, wm * G::WM + rb * 16 + (lane & 15), c0);
-        const v4f sx = *reinterpret_cast<const v4f*>(Ss + wm * G::WM + rb * 16 + (lane >> 4) * 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sxa[rb][i] = sx[i] * sw0;
-          sxb[rb][i] = sx[i] * sw1;
-        }
+      for (int tb = 0; tb < C::TBW; ++tb) {
+        const int t = wt * C::TW + tb * 16 + (lane & 15);
+        bq[tb] = lds_frag(Bs, t, c0);
+        const float sx = Ss[t];
+        f0[tb] = sx * sw0;
+        f1[tb] = sx * sw1;
       }
 #pragma unroll
-      for (int cb = 0; cb < G::CB; ++cb) {
-        const int col = (cb < 4 ? 0 : 128) + wn * 64 + (cb & 3) * 16 + (lane & 15);
-        const v8i bf = lds_frag(Bs, col, c0);
+      for (int nb = 0; nb < C::NB; ++nb) {
+        const int arow = (nb < C::NB / 2 ? wn * C::G + nb * 16 : 128 + wn * C::G + (nb - C::NB / 2) * 16) +
+                         (lane & 15);
+        const v8i aq = lds_frag(As, arow, c0);
 #pragma unroll
-        for (int rb = 0; rb < G::RB; ++rb) {
-          const v4f p = mfma_fp8(af[rb], bf);
+        for (int tb = 0; tb < C::TBW; ++tb) {
+          const v4f p = mfma_fp8(aq, bq[tb]);
+          const float f = nb < C::NB / 2 ? f0[tb] : f1[tb];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[rb][cb][i] = fmaf(p[i], cb < 4 ? sxa[rb][i] : sxb[rb][i], acc[rb][cb][i]);
+          for (int i = 0; i < 4; ++i) acc[nb][tb][i] = fmaf(p[i], f, acc[nb][tb][i]);
         }
       }
-      if (kb + 1 < kbs) MOE_LSTORE(st ^ 1);
-      __syncthreads();
+    };
+    issue(std::integral_constant<int, 0>{}, 0);
+    if (C::STAGES > 2 && 1 < kbs) issue(std::integral_constant<int, 1>{}, 1);
+    if (C::STAGES > 3 && 2 < kbs) issue(std::integral_constant<int, (C::STAGES > 3 ? 2 : 0)>{}, 2);
+    for (int kb = 0; kb < kbs; kb += C::STAGES) {
+      step(std::integral_constant<int, 0>{}, kb);
+      if (kb + 1 < kbs) step(std::integral_constant<int, 1>{}, kb + 1);
+      if (C::STAGES > 2 && kb + 2 < kbs) step(std::integral_constant<int, (C::STAGES > 2 ? 2 : 0)>{}, kb + 2);
+      if (C::STAGES > 3 && kb + 3 < kbs) step(std::integral_constant<int, (C::STAGES > 3 ? 3 : 0)>{}, kb + 3);
     }
+    __syncthreads();  // every wave is done with the ring before the epilogue reuses LDS
 
-    // ---- epilogue ---------------------------------------------------------
+    // ---- epilogue -----------------------------------------------------------
     if (FC1) {
-      // h = silu(gate) * up for this lane's 4 columns of each row
-      float* red = reinterpret_cast<float*>(smem + BM * 128);   // [2][BM] partial amax
-      float* sca = red + 2 * BM;                                // [BM] scales
-      float h[G::RB][4][4];
+      float* red = reinterpret_cast<float*>(smem);  // [WN][BT] partial amax
+      float hv[C::TBW][C::NB / 2][4];
 #pragma unroll
-      for (int rb = 0; rb < G::RB; ++rb)
+      for (int tb = 0; tb < C::TBW; ++tb) {
+        float m = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float m = 0.f;
-#pragma unroll
-          for (int c4 = 0; c4 < 4; ++c4) {
-            const float g = acc[rb][c4][i], u = acc[rb][c4 + 4][i];
-            const float hv = g / (1.0f + expf(-g)) * u;
-            h[rb][c4][i] = hv;
-            m = fmaxf(m, fabsf(hv));
-          }
-          m = group_max<16>(m);
-          if ((lane & 15) == 0) red[wn * BM + wm * G::WM + rb * 16 + (lane >> 4) * 4 + i] = m;
-        }
-      __syncthreads();
-      uint8_t* out = smem;  // [BM][128] codes
-#pragma unroll
-      for (int rb = 0; rb < G::RB; ++rb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = wm * G::WM + rb * 16 + (lane >> 4) * 4 + i;
-          const float amax = fmaxf(red[row], red[BM + row]);
-          const float s = amax / kE4m3Max;
-#pragma unroll
-          for (int c4 = 0; c4 < 4; ++c4) {
-            const float q = s == 0.f ? 0.f : h[rb][c4][i] / s;
-            const int code = s == 0.f ? 0 : (cvt2_e4m3(q, 0.f, 0, false) & 0xff);
-            out[row * 128 + wn * 64 + c4 * 16 + (lane & 15)] = (uint8_t)code;
-          }
-          if (wn == 0 && (lane & 15) == 0) sca[row] = s;
-        }
-      __syncthreads();
-      const int ikb = a.inter / 128;
-      for (int q = tid; q < BM * 8; q += kThreads) {
-        const int row = q >> 3, c = q & 7;
-        if (row < rows_valid)
-          *reinterpret_cast<u32x4*>(a.hq + (int64_t)(p0 + row) * a.inter + nt * 128 + c * 16) =
-              *reinterpret_cast<const u32x4*>(out + row * 128 + c * 16);
-      }
-      if (tid < rows_valid) a.hs[(int64_t)(p0 + tid) * ikb + nt] = sca[tid];
-    } else {
-      uint16_t* out = reinterpret_cast<uint16_t*>(smem);  // [BM][256] bf16
-#pragma unroll
-      for (int rb = 0; rb < G::RB; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < G::CB; ++cb) {
-          const int col = (cb < 4 ? 0 : 128) + wn * 64 + (cb & 3) * 16 + (lane & 15);
+        for (int g = 0; g < C::NB / 2; ++g)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int row = wm * G::WM + rb * 16 + (lane >> 4) * 4 + i;
-            out[row * kBN + col] = (uint16_t)f32_to_bf16_rne(acc[rb][cb][i]);
+            const float gt = acc[g][tb][i], up = acc[C::NB / 2 + g][tb][i];
+            const float h = gt / (1.0f + expf(-gt)) * up;
+            hv[tb][g][i] = h;
+            m = fmaxf(m, fabsf(h));
+          }
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        if (lane < 16) red[wn * BT + wt * C::TW + tb * 16 + lane] = m;
+      }
+      __syncthreads();
+      const int ikb = a.inter / 128;
+#pragma unroll
+      for (int tb = 0; tb < C::TBW; ++tb) {
+        const int t = wt * C::TW + tb * 16 + (lane & 15);
+        float amax = 0.f;
+#pragma unroll
+        for (int w = 0; w < C::WN; ++w) amax = fmaxf(amax, red[w * BT + t]);
+        const float s = amax / kE4m3Max;
+        if (t < rows_valid) {
+          uint8_t* dst = a.hq + (int64_t)(p0 + t) * a.inter + nt * 128 + wn * C::G + 4 * (lane >> 4);
+#pragma unroll
+          for (int g = 0; g < C::NB / 2; ++g) {
+            uint32_t word = 0;
+            if (s != 0.f) {
+              int w = cvt2_e4m3(hv[tb][g][0] / s, hv[tb][g][1] / s, 0, false);
+              w = cvt2_e4m3(hv[tb][g][2] / s, hv[tb][g][3] / s, w, true);
+              word = (uint32_t)w;
+            }
+            *reinterpret_cast<uint32_t*>(dst + g * 16) = word;
+          }
+          if (wn == 0 && (lane >> 4) == 0) a.hs[(int64_t)(p0 + t) * ikb + nt] = s;
+        }
+      }
+    } else {
+      const int n0 = nt * kBN;
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) {
+        const int n = (nb < C::NB / 2 ? wn * C::G + nb * 16 : 128 + wn * C::G + (nb - C::NB / 2) * 16) +
+                      4 * (lane >> 4);
+#pragma unroll
+        for (int tb = 0; tb < C::TBW; ++tb) {
+          const int t = wt * C::TW + tb * 16 + (lane & 15);
+          if (t < rows_valid && n0 + n < a.n_rows) {
+            u32x2 o;
+            o[0] = f32_to_bf16_rne(acc[nb][tb][0]) | (f32_to_bf16_rne(acc[nb][tb][1]) << 16);
+            o[1] = f32_to_bf16_rne(acc[nb][tb][2]) | (f32_to_bf16_rne(acc[nb][tb][3]) << 16);
+            *reinterpret_cast<u32x2*>(a.y + (int64_t)(p0 + t) * a.n_rows + n0 + n) = o;
           }
         }
-      __syncthreads();
-      const int n0 = nt * kBN;
-      const int ncols = min(kBN, a.n_rows - n0);
-      for (int q = tid; q < BM * 32; q += kThreads) {
-        const int row = q >> 5, c = (q & 31) * 8;
-        if (row < rows_valid && c < ncols)
-          *reinterpret_cast<u32x4*>(a.y + (int64_t)(p0 + row) * a.n_rows + n0 + c) =
-              *reinterpret_cast<const u32x4*>(out + row * kBN + c);
       }
     }
-    __syncthreads();
+    __syncthreads();  // the next tile's DMA reuses the LDS the epilogue read
   }
 }
 
-template <int BM, bool FC1>
+template <int BT, bool FC1>
 static int launch_one(const GemmArgs& a, void* stream) {
-  hipLaunchKernelGGL((gemm_fp8_kernel<BM, FC1>), dim3(a.grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream), a);
+  hipLaunchKernelGGL((gemm_fp8_kernel<BT, FC1>), dim3(a.grid), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 template <bool FC1>
-static int launch_bm(const GemmArgs& a, int block_m, void* stream) {
+static int launch_bt(const GemmArgs& a, int block_m, void* stream) {
   switch (block_m) {
+    case 16: return launch_one<16, FC1>(a, stream);
     case 32: return launch_one<32, FC1>(a, stream);
     case 64: return launch_one<64, FC1>(a, stream);
     case 128: return launch_one<128, FC1>(a, stream);
@@ -307,21 +373,24 @@ static int launch_bm(const GemmArgs& a, int block_m, void* stream) {
   return -1;
 }
 
-int launch_fc1(const GemmArgs& a, int block_m, void* stream) { return launch_bm<true>(a, block_m, stream); }
-int launch_fc2(const GemmArgs& a, int block_m, void* stream) { return launch_bm<false>(a, block_m, stream); }
+int launch_fc1(const GemmArgs& a, int block_m, void* stream) { return launch_bt<true>(a, block_m, stream); }
+int launch_fc2(const GemmArgs& a, int block_m, void* stream) { return launch_bt<false>(a, block_m, stream); }
 
-template <int BM, bool FC1>
+template <int BT, bool FC1>
 static int occ() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_fp8_kernel<BM, FC1>, kThreads, 0) != hipSuccess) return 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_fp8_kernel<BT, FC1>, kThreads, 0) != hipSuccess) return 1;
   return n > 0 ? n : 1;
 }
 
 int gemm_max_workgroups_per_cu(int which, int block_m) {
-  if (which == 1) {
-    switch (block_m) { case 32: return occ<32, true>(); case 64: return occ<64, true>(); default: return occ<128, true>(); }
+  const bool f1 = which == 1;
+  switch (block_m) {
+    case 16: return f1 ? occ<16, true>() : occ<16, false>();
+    case 32: return f1 ? occ<32, true>() : occ<32, false>();
+    case 64: return f1 ? occ<64, true>() : occ<64, false>();
+    default: return f1 ? occ<128, true>() : occ<128, false>();
   }
-  switch (block_m) { case 32: return occ<32, false>(); case 64: return occ<64, false>(); default: return occ<128, false>(); }
 }
 
 }  // namespace moe

@@ -43,8 +43,8 @@ moe_status_t validate_config(const moe_config_t* cfg, int32_t expected_m, int32_
   if (cfg->hidden % 128 || cfg->intermediate % 128)
     return fail(MOE_ERR_UNSUPPORTED, "hidden (%d) and intermediate (%d) must be multiples of 128",
                 cfg->hidden, cfg->intermediate);
-  if (cfg->hidden > 65536 || cfg->intermediate > 65536)
-    return fail(MOE_ERR_UNSUPPORTED, "hidden/intermediate above 65536 are not supported");
+  if (cfg->hidden > 16384 || cfg->intermediate > 16384)
+    return fail(MOE_ERR_UNSUPPORTED, "hidden/intermediate above 16384 are not supported");
   if (cfg->num_experts < 1 || cfg->num_experts > kMaxExperts)
     return fail(MOE_ERR_UNSUPPORTED, "num_experts %d outside [1, %d]", cfg->num_experts, kMaxExperts);
   if (!valid_top_k(cfg->top_k))
@@ -73,21 +73,17 @@ moe_status_t validate_config(const moe_config_t* cfg, int32_t expected_m, int32_
   return MOE_OK;
 }
 
-// Tile tactic from the expected rows per expert.  block_m follows the token
-// bucket; weights always come in 256-row tiles (FC1: 128 gate + 128 up rows
-// of one 128-wide output block; FC2: two 128-row blocks of H).
+// Tile tactic from the expected rows per expert: the token tile (block_m)
+// is the token bucket, clamped to [16, 128].  Weights always come in 256-row
+// tiles (FC1: 128 gate + 128 up rows of one 128-wide block of h; FC2: two
+// 128-row blocks of H).
 Tactic choose_tactic(const moe_config_t& cfg, int32_t expected_m) {
   (void)cfg;
   Tactic t;
   t.bucket = token_bucket(expected_m);
   t.block_n = 256;
-  t.stages = 2;
-  if (t.bucket <= 32)
-    t.block_m = 32;
-  else if (t.bucket <= 64)
-    t.block_m = 64;
-  else
-    t.block_m = 128;
+  t.block_m = t.bucket <= 16 ? 16 : (t.bucket >= 128 ? 128 : t.bucket);
+  t.stages = t.block_m == 64 ? 3 : (t.block_m == 128 ? 3 : 4);
   return t;
 }
 
