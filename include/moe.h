@@ -137,7 +137,9 @@ enum {
   MOE_REGION_HQ = 9,            /* FC1 output rows [row_cap, I]: e4m3 (bf16 for MXFP8) */
   MOE_REGION_HS = 10,           /* float32 [row_cap, I/128] (FP8 path) */
   MOE_REGION_Y = 11,            /* bf16 [row_cap, H] un-weighted FC2 rows */
-  MOE_REGION_TILES = 12         /* int32 [max_m_tiles, 2] (expert, first sorted row) */
+  MOE_REGION_TILES = 12,        /* int32 [max_m_tiles, 2] (expert, first sorted row) */
+  MOE_REGION_W13T = 13,         /* e4m3 w13 tiled at create: [E, I/128, H/128] tiles of 32 KB */
+  MOE_REGION_W2T = 14           /* e4m3 w2 tiled at create: [E, ceil(H/256), I/128] tiles of 32 KB */
 };
 
 /* Kernel classes timed by the optional profiler. */
@@ -167,10 +169,15 @@ moe_status_t moe_workspace_query(const moe_config_t* cfg, int32_t expected_m, in
 
 /* Bind the static weights and the workspace (PR #4069, Contracts: the
  * construction of the stateful variant binds transformed static weights).
- *  cfg, w          [host in] copied; weight pointers must stay valid.
+ *  cfg, w          [host in] copied.
  *  workspace       device, 256-byte aligned, ws_bytes >= moe_workspace_query().
+ *  stream          the weight transform is launched on it.
  *  out             [host out] new handle (host memory owned by the library).
- * Launches nothing: the kernels read the weights in the layout above. */
+ * Launches one transform per weight tensor that copies the e4m3 codes into
+ * the workspace in the kernels' tile order (MOE_REGION_W13T / W2T); the
+ * scale tensors are read in place.  The caller keeps the scale tensors alive
+ * and unchanged while the handle exists; the e4m3 tensors may be released
+ * once the stream has passed the create call. */
 moe_status_t moe_layer_create(const moe_config_t* cfg, int32_t expected_m, int32_t max_rows,
                               float capacity_factor, const moe_weights_t* w, void* workspace,
                               size_t ws_bytes, void* stream, moe_layer_t** out);

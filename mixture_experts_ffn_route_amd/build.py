@@ -29,6 +29,7 @@ SOURCES = [
     "moe_compact.hip",
     "moe_gemm_fp8.hip",
     "moe_combine.hip",
+    "moe_weights.hip",
 ]
 
 # Packed FP32 VALU ops are disabled for all device code.

@@ -80,7 +80,6 @@ moe_status_t hip_fail(const char* what) {
 extern "C" moe_status_t moe_layer_create(const moe_config_t* cfg, int32_t expected_m, int32_t max_rows,
                                          float capacity_factor, const moe_weights_t* w, void* workspace,
                                          size_t ws_bytes, void* stream, moe_layer_t** out) {
-  (void)stream;
   moe::clear_error();
   moe_status_t s = moe::validate_config(cfg, expected_m, max_rows, capacity_factor);
   if (s != MOE_OK) return s;
@@ -124,6 +123,16 @@ extern "C" moe_status_t moe_layer_create(const moe_config_t* cfg, int32_t expect
   };
   l->grid_fc1 = grid(1);
   l->grid_fc2 = grid(2);
+  // weight codes -> kernel tile order, stream-ordered before any forward
+  uint8_t* w13t = l->ws + L.off[MOE_REGION_W13T];
+  uint8_t* w2t = l->ws + L.off[MOE_REGION_W2T];
+  if (moe::launch_tile_weights(static_cast<const uint8_t*>(w->w13), w13t, cfg->num_experts, 2 * cfg->intermediate,
+                               cfg->hidden, cfg->intermediate / 128, cfg->intermediate, true, stream) != 0 ||
+      moe::launch_tile_weights(static_cast<const uint8_t*>(w->w2), w2t, cfg->num_experts, cfg->hidden,
+                               cfg->intermediate, (cfg->hidden + 255) / 256, cfg->intermediate, false, stream) != 0) {
+    delete l;
+    return hip_fail("weight transform launch");
+  }
   l->prof = false;
   memset(l->ms, 0, sizeof(l->ms));
   memset(l->launches, 0, sizeof(l->launches));
@@ -209,7 +218,7 @@ extern "C" moe_status_t moe_layer_forward(moe_layer_t* l, void* stream) {
   g1.a_mode = (c.flags & MOE_FLAG_PER_ROUTE_STAGING) ? 2 : 1;
   g1.sorted_route = ca.sorted_route;
   g1.top_k = c.top_k;
-  g1.w = static_cast<const uint8_t*>(l->w.w13);
+  g1.w = region<uint8_t>(l, MOE_REGION_W13T);
   g1.w_scale = static_cast<const float*>(l->w.w13_scale);
   g1.n_rows = 2 * c.intermediate;
   g1.k_dim = c.hidden;
@@ -232,7 +241,7 @@ extern "C" moe_status_t moe_layer_forward(moe_layer_t* l, void* stream) {
   g2.a_mode = 0;
   g2.sorted_route = ca.sorted_route;
   g2.top_k = c.top_k;
-  g2.w = static_cast<const uint8_t*>(l->w.w2);
+  g2.w = region<uint8_t>(l, MOE_REGION_W2T);
   g2.w_scale = static_cast<const float*>(l->w.w2_scale);
   g2.n_rows = c.hidden;
   g2.k_dim = c.intermediate;
@@ -276,7 +285,7 @@ extern "C" moe_status_t moe_read_status(moe_layer_t* l, void* stream, uint32_t* 
 extern "C" moe_status_t moe_layer_region(moe_layer_t* l, int32_t r, void** dptr, size_t* bytes) {
   moe::clear_error();
   if (!l || !dptr || !bytes) return moe::fail(MOE_ERR_INVALID_ARG, "NULL argument");
-  if (r < 0 || r > MOE_REGION_TILES) return moe::fail(MOE_ERR_INVALID_ARG, "unknown region %d", r);
+  if (r < 0 || r > MOE_REGION_W2T) return moe::fail(MOE_ERR_INVALID_ARG, "unknown region %d", r);
   *dptr = l->ws + l->L.off[r];
   *bytes = l->L.size[r];
   return MOE_OK;

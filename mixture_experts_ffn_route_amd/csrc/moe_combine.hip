@@ -10,46 +10,55 @@
 
 namespace moe {
 
-// One wave per token; each lane reduces 8 consecutive columns per pass
-// (16-byte loads and stores, 512 columns per wave pass).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// One thread per (token, 8 consecutive columns): the K route rows are loaded
+// first (16 bytes each, independent), then reduced in ascending slot order.
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.tokens) return;
-  const int lane = threadIdx.x & 63;
+  const int chunks = a.hidden >> 3;
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= (int64_t)a.tokens * chunks) return;
+  const int64_t t = g / chunks;
+  const int c = (int)(g - t * chunks) * 8;
   const int K = a.top_k;
-  int64_t pos[8];
   float w[8];
-  for (int k = 0; k < K; ++k) {
-    const int p = a.route_pos[(int64_t)t * K + k];
-    pos[k] = p;
-    w[k] = p >= 0 ? a.staged_w[(int64_t)t * K + k] : 0.0f;
-  }
-  for (int c = lane * 8; c < a.hidden; c += 512) {
-    float acc[8];
+  u32x4 raw[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-    for (int k = 0; k < K; ++k) {
-      if (pos[k] < 0) continue;
-      const uint4 raw = *reinterpret_cast<const uint4*>(a.y + pos[k] * a.hidden + c);
-      const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = fmaf(w[k], bf16_to_f32(u[i] & 0xffffu), acc[2 * i]);
-        acc[2 * i + 1] = fmaf(w[k], bf16_to_f32(u[i] >> 16), acc[2 * i + 1]);
+  for (int k = 0; k < 8; ++k) {
+    w[k] = 0.f;
+    raw[k] = u32x4{0u, 0u, 0u, 0u};
+    if (k < K) {
+      const int p = a.route_pos[t * K + k];
+      if (p >= 0) {
+        w[k] = a.staged_w[t * K + k];
+        raw[k] = *reinterpret_cast<const u32x4*>(a.y + (int64_t)p * a.hidden + c);
       }
     }
-    uint4 o;
-    o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
-    o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
-    o.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
-    o.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
-    *reinterpret_cast<uint4*>(a.out + (int64_t)t * a.hidden + c) = o;
   }
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (k < K) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(w[k], bf16_to_f32(raw[k][i] & 0xffffu), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(w[k], bf16_to_f32(raw[k][i] >> 16), acc[2 * i + 1]);
+      }
+    }
+  }
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16_rne(acc[2 * i]) | (f32_to_bf16_rne(acc[2 * i + 1]) << 16);
+  *reinterpret_cast<u32x4*>(a.out + t * a.hidden + c) = o;
 }
 
 int launch_combine(const CombineArgs& a, void* stream) {
   if (a.tokens <= 0) return 0;
-  hipLaunchKernelGGL(combine_kernel, dim3((a.tokens + 3) / 4), dim3(256), 0, static_cast<hipStream_t>(stream), a);
+  const int64_t threads = (int64_t)a.tokens * (a.hidden / 8);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -24,10 +24,13 @@
 //    SwiGLU and the 1x128 amax of the epilogue see whole blocks; FC2's are
 //    two 128-row blocks of H.
 //  * K-blocks move global -> LDS by LDS-DMA (global_load_lds_dwordx4), a
-//    multi-stage ring, no staging registers.  The source address of each
-//    lane is chosen so the 16-byte chunks land XOR-swizzled by row, which
-//    keeps the MFMA operand reads free of bank conflicts.  FC1 gathers its
-//    token rows through the sorted route list (one staged row per token).
+//    multi-stage ring, no staging registers.  Both operands land in LDS in
+//    MFMA fragment order (16-row block x {lo, hi} x 64 lanes x 16 bytes), so
+//    every operand read is one lane-linear 1 KB ds_read_b128 (no bank
+//    conflicts, no address math).  Weights were tiled in that order at create
+//    time, so a weight K-block is one contiguous 32 KB copy; token rows are
+//    gathered per lane (FC1 through the sorted route list: one staged row per
+//    token).
 //  * Persistent workgroups: the (token tile, column tile) space is split into
 //    eight contiguous ranges, one per XCD (workgroup i runs on XCD i % 8), so
 //    neighbouring tiles on an XCD share rows and weights in its L2.
@@ -55,28 +58,27 @@ constexpr int kMaxKBlocks = 128;  // K <= 16384
 constexpr int kWsBytes = 2 * kMaxKBlocks * 4;  // per-tile weight-scale columns
 constexpr int kRingBytes = kLdsBytes - kWsBytes;
 
-// Physical 16-byte chunk of logical chunk c in row r.  Rows r..r+7 and the
-// even/odd rows of r..r+15 all land on distinct chunk positions.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r & 1) << 2) ^ ((r >> 1) & 7)); }
-
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b) {
   const v4f z = {0.f, 0.f, 0.f, 0.f};
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
 }
 
-// The 32 K-bytes lane l contributes to a 16x16x128 MFMA: row (l % 16),
-// logical chunks 2*(l/16) and 2*(l/16)+1.
-__device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int row, int c0) {
-  const uint8_t* base = tile + row * kKB;
-  const u32x4 lo = *reinterpret_cast<const u32x4*>(base + (swz(row, c0) << 4));
-  const u32x4 hi = *reinterpret_cast<const u32x4*>(base + (swz(row, c0 + 1) << 4));
+// LDS is addressed through 32-bit address-space-3 pointers throughout: no
+// generic-pointer casts, so offsets fold into instruction immediates.
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) const float lds_f32;
+
+// Operand of a 16x16x128 MFMA from a fragment-ordered LDS tile: block `blk`
+// (16 rows) holds its "lo" 1 KB then its "hi" 1 KB, lane-linear.
+__device__ __forceinline__ v8i lds_frag(const lds_u8* tile, int blk, int lane) {
+  const u32x4 lo = *reinterpret_cast<lds_u32x4*>(tile + ((blk * 2) * 64 + lane) * 16);
+  const u32x4 hi = *reinterpret_cast<lds_u32x4*>(tile + ((blk * 2 + 1) * 64 + lane) * 16);
   v8i r;
   r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];
   r[4] = (int)hi[0]; r[5] = (int)hi[1]; r[6] = (int)hi[2]; r[7] = (int)hi[3];
   return r;
 }
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // LDS-DMA (global_load_lds): lane L's bytes land at lds_wave_base + L * size;
 // lds_wave_base is wave-uniform and goes through M0.  Issued as inline asm so
@@ -84,14 +86,12 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // fills across the loop back-edge, never drains the ring; the K loop waits
 // on the vector-memory counter itself.  The "memory" clobber keeps every LDS
 // access in program order around these instructions.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)p);
-}
-__device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* lds_wave_base) {
+__device__ __forceinline__ uint32_t lds_addr(const lds_u8* p) { return (uint32_t)(uintptr_t)p; }
+__device__ __forceinline__ void dma16(const uint8_t* src, const lds_u8* lds_wave_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(src), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(const float* src, uint8_t* lds_wave_base) {
+__device__ __forceinline__ void dma4(const float* src, const lds_u8* lds_wave_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                :: "v"(src), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
 }
@@ -138,18 +138,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring2[C::STAGES > 2 ? C::STAGE : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t ring3[C::STAGES > 3 ? C::STAGE : 16];
   __shared__ __attribute__((aligned(16))) float wsc[2 * kMaxKBlocks];  // [block 0 | block 1][kb]
-  auto ring = [&](auto stage) -> uint8_t* {
+  auto ring = [&](auto stage) -> lds_u8* {
     constexpr int S = decltype(stage)::value;
-    if constexpr (S == 0) return ring0;
-    else if constexpr (S == 1) return ring1;
-    else if constexpr (S == 2) return ring2;
-    else return ring3;
+    if constexpr (S == 0) return (lds_u8*)ring0;
+    else if constexpr (S == 1) return (lds_u8*)ring1;
+    else if constexpr (S == 2) return (lds_u8*)ring2;
+    else return (lds_u8*)ring3;
   };
   uint8_t* smem = ring0;  // epilogue scratch
+  const lds_f32* wscl = (const lds_f32*)wsc;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave % C::WN, wt = wave / C::WN;
   const int kbs = a.k_dim / kKB;
   const int nblk_w = a.n_rows / 128;
@@ -159,7 +160,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
   const int slot = blockIdx.x >> 3;
   const int per_xcd = gridDim.x >> 3;
   const int64_t v_begin = total * xcd / 8, v_end = total * (xcd + 1) / 8;
-  const int c0 = (lane >> 4) * 2;
 
   for (int64_t v = v_begin + slot; v < v_end; v += per_xcd) {
     // ---- tile coordinates ------------------------------------------------
@@ -184,26 +184,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
     }
 
     // ---- per-lane DMA sources -------------------------------------------
-    const uint8_t* a_src[C::A_INSTR];
-#pragma unroll
-    for (int j = 0; j < C::A_INSTR; ++j) {
-      const int q = wave * (C::A_INSTR * 64) + j * 64 + lane;
-      const int row = q >> 3;
-      const int wrow = (row < 128 ? nb0 * 128 + row : nb1 * 128 + row - 128);
-      a_src[j] = a.w + ((int64_t)e * a.n_rows + wrow) * a.k_dim + (swz(row, q & 7) << 4);
-    }
+    // weights: the tile's K-blocks are contiguous 32 KB pieces
+    const uint8_t* a_src =
+        a.w + ((int64_t)e * a.n_tiles + nt) * kbs * (int64_t)C::A_BYTES + (wave * C::A_INSTR * 64 + lane) * 16;
     auto src_row = [&](int t) -> int64_t {
       const int p = p0 + min(t, rows_valid - 1);
       if (!FC1) return p;
       const int r = a.sorted_route[p];
       return a.a_mode == 2 ? r : r / a.top_k;
     };
+    // tokens: virtual lane V of the tile covers fragment piece V/64
     const uint8_t* b_src[C::B_INSTR];
 #pragma unroll
     for (int j = 0; j < C::B_INSTR; ++j) {
-      const int q = wave * BT + j * 64 + (lane < C::B_LANES ? lane : 0);
-      const int row = q >> 3;
-      b_src[j] = a.a + src_row(row) * a.k_dim + (swz(row, q & 7) << 4);
+      const int v = wave * BT + j * 64 + (lane < C::B_LANES ? lane : 0);
+      const int piece = v >> 6, lp = v & 63;
+      const int t = (piece >> 1) * 16 + (lp & 15);
+      const int chunk = 2 * (lp >> 4) + (piece & 1);
+      b_src[j] = a.a + src_row(t) * a.k_dim + chunk * 16;
     }
     const float* s_src = a.a_scale + src_row(wave * C::S_LANES + (lane < C::S_LANES ? lane : 0)) * kbs;
     // this tile's two weight-scale columns, DMA'd once per tile (waves 0-3)
@@ -212,16 +210,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
       const int kb = half * 64 + lane;
       if (kb < kbs)
         dma4(a.w_scale + ((int64_t)e * nblk_w + (blk ? nb1 : nb0)) * kbs + kb,
-             reinterpret_cast<uint8_t*>(wsc) + (blk * kMaxKBlocks + half * 64) * 4);
+             (const lds_u8*)wsc + (blk * kMaxKBlocks + half * 64) * 4);
     }
 
     auto issue = [&](auto stage, int kb) {
-      uint8_t* As = ring(stage);
-      uint8_t* Bs = As + C::A_BYTES;
-      uint8_t* Ss = Bs + C::B_BYTES;
+      const lds_u8* As = ring(stage);
+      const lds_u8* Bs = As + C::A_BYTES;
+      const lds_u8* Ss = Bs + C::B_BYTES;
 #pragma unroll
       for (int j = 0; j < C::A_INSTR; ++j)
-        dma16(a_src[j] + kb * kKB, As + (wave * (C::A_INSTR * 64) + j * 64) * 16);
+        dma16(a_src + (int64_t)kb * C::A_BYTES + j * 1024, As + (wave * C::A_INSTR + j) * 1024);
 #pragma unroll
       for (int j = 0; j < C::B_INSTR; ++j)
         if (lane < C::B_LANES) dma16(b_src[j] + kb * kKB, Bs + (wave * BT + j * 64) * 16);
@@ -250,25 +248,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
       if (kb + C::STAGES - 1 < kbs)
         issue(std::integral_constant<int, (ST + C::STAGES - 1) % C::STAGES>{}, kb + C::STAGES - 1);
 
-      const uint8_t* As = ring(stage);
-      const uint8_t* Bs = As + C::A_BYTES;
-      const float* Ss = reinterpret_cast<const float*>(Bs + C::B_BYTES);
-      const float sw0 = wsc[kb], sw1 = wsc[kMaxKBlocks + kb];
+      const lds_u8* As = ring(stage);
+      const lds_u8* Bs = As + C::A_BYTES;
+      const lds_f32* Ss = (const lds_f32*)(Bs + C::B_BYTES);
+      const float sw0 = wscl[kb], sw1 = wscl[kMaxKBlocks + kb];
       v8i bq[C::TBW];
       float f0[C::TBW], f1[C::TBW];
 #pragma unroll
       for (int tb = 0; tb < C::TBW; ++tb) {
-        const int t = wt * C::TW + tb * 16 + (lane & 15);
-        bq[tb] = lds_frag(Bs, t, c0);
-        const float sx = Ss[t];
+        const int tblk = wt * C::TBW + tb;
+        bq[tb] = lds_frag(Bs, tblk, lane);
+        const float sx = Ss[tblk * 16 + (lane & 15)];
         f0[tb] = sx * sw0;
         f1[tb] = sx * sw1;
       }
+      // Weight fragments stream one block ahead; the scheduling barrier keeps
+      // the compiler from hoisting every block's LDS reads to the top, which
+      // would hold all of them in registers at once.
+      auto rblk = [&](int nb) {
+        return nb < C::NB / 2 ? wn * (C::G / 16) + nb : 8 + wn * (C::G / 16) + (nb - C::NB / 2);
+      };
+      v8i aq = lds_frag(As, rblk(0), lane);
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb) {
-        const int arow = (nb < C::NB / 2 ? wn * C::G + nb * 16 : 128 + wn * C::G + (nb - C::NB / 2) * 16) +
-                         (lane & 15);
-        const v8i aq = lds_frag(As, arow, c0);
+        const v8i an = lds_frag(As, rblk(nb + 1 < C::NB ? nb + 1 : nb), lane);
 #pragma unroll
         for (int tb = 0; tb < C::TBW; ++tb) {
           const v4f p = mfma_fp8(aq, bq[tb]);
@@ -276,6 +279,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[nb][tb][i] = fmaf(p[i], f, acc[nb][tb][i]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        aq = an;
       }
     };
     issue(std::integral_constant<int, 0>{}, 0);

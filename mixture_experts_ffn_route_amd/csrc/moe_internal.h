@@ -11,8 +11,8 @@ namespace moe {
 
 constexpr int kMaxExperts = 1024;
 constexpr int kCompactChunk = 4096;  // routes per compaction workgroup (256 lanes x 16)
-constexpr int kNumRegions = 14;
-constexpr int kRegionBlkBase = 13;   // internal: per-(compaction block, expert) bases
+constexpr int kNumRegions = 16;
+constexpr int kRegionBlkBase = 15;   // internal: per-(compaction block, expert) bases
 
 // Words of the device header (MOE_REGION_STATUS).
 enum HeaderWord : int {
@@ -93,7 +93,7 @@ struct GemmArgs {
   int32_t a_mode;          // 0: sorted position p; 1: token = route/K; 2: route id
   const int32_t* sorted_route;
   int32_t top_k;
-  // B operand: expert weights [E, N, K]
+  // B operand: expert weights tiled by moe_weights.hip ([E, n_tiles, K/128] x 32 KB)
   const uint8_t* w;
   const float* w_scale;    // [E, N/128, K/128]
   int32_t n_rows;          // N (2I for FC1, H for FC2)
@@ -121,5 +121,8 @@ struct CombineArgs {
   uint16_t* out;
 };
 int launch_combine(const CombineArgs& a, void* stream);
+
+int launch_tile_weights(const uint8_t* src, uint8_t* dst, int experts, int n_rows, int k_dim, int n_tiles,
+                        int inter, bool fc1, void* stream);
 
 }  // namespace moe

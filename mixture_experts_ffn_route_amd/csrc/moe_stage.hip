@@ -72,17 +72,24 @@ __global__ __launch_bounds__(256) void stage_routes_kernel(StageArgs a) {
   int ids[8];
   float ws[8];
   bool act[8];
-  for (int k = 0; k < K; ++k) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
     ids[k] = -1;
     ws[k] = 0.0f;
     act[k] = false;
   }
   if (t < a.tokens) {
-    for (int k = 0; k < K; ++k) {
-      const int e = a.topk_idx[(int64_t)t * K + k];
-      const float w = a.topk_w[(int64_t)t * K + k];
-      ids[k] = e;
-      ws[k] = w;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {  // all loads first
+      if (k < K) {
+        ids[k] = a.topk_idx[(int64_t)t * K + k];
+        ws[k] = a.topk_w[(int64_t)t * K + k];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k >= K) continue;
+      const int e = ids[k];
       if (e == -1) continue;
       if (e < -1 || e >= a.num_experts) {
         bits |= MOE_DEV_BAD_EXPERT;
@@ -91,8 +98,10 @@ __global__ __launch_bounds__(256) void stage_routes_kernel(StageArgs a) {
       act[k] = true;
     }
     if (a.flags & MOE_FLAG_CHECK_ROUTES) {
-      for (int k = 1; k < K; ++k) {
-        if (!act[k]) continue;
+#pragma unroll
+      for (int k = 1; k < 8; ++k) {
+        if (k >= K || !act[k]) continue;
+#pragma unroll
         for (int j = 0; j < k; ++j) {
           if (act[j] && ids[j] == ids[k]) {  // the lowest slot of an id stays active
             act[k] = false;
@@ -101,7 +110,8 @@ __global__ __launch_bounds__(256) void stage_routes_kernel(StageArgs a) {
           }
         }
       }
-      for (int k = 0; k < K; ++k) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
         if (act[k] && !isfinite(ws[k])) {
           act[k] = false;
           bits |= MOE_DEV_NONFINITE;
@@ -109,9 +119,12 @@ __global__ __launch_bounds__(256) void stage_routes_kernel(StageArgs a) {
       }
     }
   }
-  for (int k = 0; k < K; ++k) {
-    a.staged_idx[(int64_t)t * K + k] = act[k] ? ids[k] : -1;
-    a.staged_w[(int64_t)t * K + k] = act[k] ? ws[k] : 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (k < K) {
+      a.staged_idx[(int64_t)t * K + k] = act[k] ? ids[k] : -1;
+      a.staged_w[(int64_t)t * K + k] = act[k] ? ws[k] : 0.0f;
+    }
   }
   if (bits) atomicOr(a.hdr + kHdrStatus, bits);
 }

@@ -224,3 +224,42 @@ def test_dsv3_shape_sampled():
 @pytest.mark.slow
 def test_skewed_zipf_sampled():
     _sampled_full_size(CONFIGS["skewed"], 0, 24, "zipf T=8192")
+
+
+def _retile(w, fc1, inter):
+    """NumPy statement of the kernels' weight tile order (see moe_weights.hip)."""
+    E, N, K = w.shape
+    n_tiles = inter // 128 if fc1 else (N + 255) // 256
+    kbs = K // 128
+    out = np.zeros((E, n_tiles, kbs, 16, 2, 64, 16), np.uint8)
+    lane = np.arange(64)
+    for nt in range(n_tiles):
+        for rb in range(16):
+            if fc1:
+                rows = (nt * 128 + rb * 16 if rb < 8 else inter + nt * 128 + (rb - 8) * 16) + (lane % 16)
+            else:
+                rows = nt * 256 + rb * 16 + (lane % 16)
+            valid = rows < N
+            for kb in range(kbs):
+                for hilo in range(2):
+                    kbyte = kb * 128 + 32 * (lane // 16) + 16 * hilo
+                    idx = kbyte[:, None] + np.arange(16)[None, :]
+                    vals = w[:, np.minimum(rows, N - 1)[:, None], idx]  # [E, 64, 16]
+                    out[:, nt, kb, rb, hilo] = np.where(valid[None, :, None], vals, 0)
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("shape", [CONFIGS["tiny"], MoEShape(16, 384, 256, 4, 2, "topk")])
+def test_create_time_weight_tiling_is_exact(shape):
+    inp = make_layer_inputs(shape, seed=8)
+    dev = to_device(inp)
+    layer = make_layer(shape, dev)
+    torch.cuda.synchronize()
+    w13t = _np(layer.region("w13t", torch.uint8))
+    w2t = _np(layer.region("w2t", torch.uint8))
+    assert np.array_equal(w13t, _retile(inp.w13, True, shape.intermediate))
+    assert np.array_equal(w2t, _retile(inp.w2, False, shape.intermediate))
+    run = run_forward(layer, dev)
+    torch.cuda.synchronize()
+    res = M.forward_fp8(inp.x_bf16, inp.topk_idx, inp.topk_w, inp.w13, inp.w13_scale, inp.w2, inp.w2_scale)
+    assert_output_close(_bits(run), res.out_bits, f"H={shape.hidden}")
