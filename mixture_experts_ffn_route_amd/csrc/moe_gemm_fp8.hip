@@ -12,14 +12,16 @@
 // Limitations.
 //
 // Design (CDNA4):
-//  * One K-block of 128 is exactly one v_mfma_f32_16x16x128_f8f6f4.  Its FP32
-//    result is promoted into an accumulator held in architectural VGPRs with
-//    one FMA by sx[token] * s_w[block] per output per K-block.
+//  * One K-block of 128 is exactly one v_mfma_f32_16x16x128_f8f6f4.  The
+//    block scales are applied by keeping the accumulator divided by the
+//    current block's scale product (see carry_scale): one multiply per output
+//    per K-block rescales it and the MFMA accumulates in place, so no MFMA
+//    result needs registers of its own.
 //  * Weights are the MFMA row operand and tokens the column operand, so a
 //    lane's four outputs of a 16x16 block share one token and one weight
 //    block: one scale product per lane per token block.
 //  * Workgroup tile: 256 weight rows x BT tokens, 8 waves (two per SIMD, so
-//    one wave's promotion FMAs run beside the other's MFMAs).  FC1's 256
+//    one wave's rescaling multiplies run beside the other's MFMAs).  FC1's 256
 //    weight rows are the gate and up rows of one 128-wide block of h, so the
 //    SwiGLU and the 1x128 amax of the epilogue see whole blocks; FC2's are
 //    two 128-row blocks of H.
@@ -58,9 +60,18 @@ constexpr int kMaxKBlocks = 128;  // K <= 16384
 constexpr int kWsBytes = 2 * kMaxKBlocks * 4;  // per-tile weight-scale columns
 constexpr int kRingBytes = kLdsBytes - kWsBytes;
 
-__device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b) {
-  const v4f z = {0.f, 0.f, 0.f, 0.f};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
+__device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Scale product of one K-block for the promotion recursion.  The accumulator
+// is kept divided by the current block's product F = sx * sw:
+//   acc_kb = acc_{kb-1} * (F_{kb-1} / F_kb) + sum_k a*b     (MFMA with C input)
+// and multiplied by the last F after the K loop, which equals
+// sum_kb F_kb * sum_k a*b.  A block whose F is zero or subnormal carries the
+// previous F (its product is zero: its codes are all zero).
+__device__ __forceinline__ float carry_scale(float f, float prev) {
+  return fabsf(f) >= 0x1p-100f ? f : prev;
 }
 
 // LDS is addressed through 32-bit address-space-3 pointers throughout: no
@@ -69,11 +80,12 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) const float lds_f32;
 
-// Operand of a 16x16x128 MFMA from a fragment-ordered LDS tile: block `blk`
-// (16 rows) holds its "lo" 1 KB then its "hi" 1 KB, lane-linear.
-__device__ __forceinline__ v8i lds_frag(const lds_u8* tile, int blk, int lane) {
-  const u32x4 lo = *reinterpret_cast<lds_u32x4*>(tile + ((blk * 2) * 64 + lane) * 16);
-  const u32x4 hi = *reinterpret_cast<lds_u32x4*>(tile + ((blk * 2 + 1) * 64 + lane) * 16);
+// Operand of a 16x16x128 MFMA from a fragment-ordered LDS tile: each 16-row
+// block holds its "lo" 1 KB then its "hi" 1 KB, lane-linear.  `p` points at
+// this lane's 16 bytes of the block's lo half (block*2048 + lane*16).
+__device__ __forceinline__ v8i lds_frag(const lds_u8* p) {
+  const u32x4 lo = *reinterpret_cast<lds_u32x4*>(p);
+  const u32x4 hi = *reinterpret_cast<lds_u32x4*>(p + 1024);
   v8i r;
   r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];
   r[4] = (int)hi[0]; r[5] = (int)hi[1]; r[6] = (int)hi[2]; r[7] = (int)hi[3];
@@ -108,7 +120,7 @@ __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" :::
 
 template <int BT>
 struct Cfg {
-  static constexpr int WN = BT >= 64 ? 2 : (BT == 32 ? 4 : 8);  // waves along weight rows
+  static constexpr int WN = BT >= 256 ? 4 : (BT >= 64 ? 2 : (BT == 32 ? 4 : 8));  // waves along weight rows
   static constexpr int WT = kWaves / WN;                          // waves along tokens
   static constexpr int G = 128 / WN;                              // rows of each 128-row block per wave
   static constexpr int NB = 2 * G / 16;                           // 16-row weight blocks per wave
@@ -160,6 +172,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
   const int slot = blockIdx.x >> 3;
   const int per_xcd = gridDim.x >> 3;
   const int64_t v_begin = total * xcd / 8, v_end = total * (xcd + 1) / 8;
+  // lane's offset of its first weight block, token block and token scale
+  const uint32_t a_lane = (uint32_t)(wn * (C::G / 16)) * 2048u + (uint32_t)lane * 16u;
+  const uint32_t b_lane = (uint32_t)(wt * C::TBW) * 2048u + (uint32_t)lane * 16u;
+  const uint32_t s_lane = (uint32_t)(wt * C::TBW * 16 + (lane & 15));
 
   for (int64_t v = v_begin + slot; v < v_end; v += per_xcd) {
     // ---- tile coordinates ------------------------------------------------
@@ -227,10 +243,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
     };
 
     v4f acc[C::NB][C::TBW];
+    float fs0[C::TBW], fs1[C::TBW];  // current scale product per token block (gate/first, up/second)
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
       for (int tb = 0; tb < C::TBW; ++tb) acc[nb][tb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tb = 0; tb < C::TBW; ++tb) fs0[tb] = fs1[tb] = 1.0f;
 
     // ---- K loop: STAGES-deep LDS ring -------------------------------------
     auto step = [&](auto stage, int kb) {
@@ -252,35 +271,64 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
       const lds_u8* Bs = As + C::A_BYTES;
       const lds_f32* Ss = (const lds_f32*)(Bs + C::B_BYTES);
       const float sw0 = wscl[kb], sw1 = wscl[kMaxKBlocks + kb];
-      v8i bq[C::TBW];
-      float f0[C::TBW], f1[C::TBW];
-#pragma unroll
-      for (int tb = 0; tb < C::TBW; ++tb) {
-        const int tblk = wt * C::TBW + tb;
-        bq[tb] = lds_frag(Bs, tblk, lane);
-        const float sx = Ss[tblk * 16 + (lane & 15)];
-        f0[tb] = sx * sw0;
-        f1[tb] = sx * sw1;
-      }
-      // Weight fragments stream one block ahead; the scheduling barrier keeps
-      // the compiler from hoisting every block's LDS reads to the top, which
-      // would hold all of them in registers at once.
-      auto rblk = [&](int nb) {
-        return nb < C::NB / 2 ? wn * (C::G / 16) + nb : 8 + wn * (C::G / 16) + (nb - C::NB / 2);
+      // Per-lane operand bases (wave/lane part computed once per kernel):
+      // every fragment read below is base + compile-time offset.
+      const lds_u8* Ap = As + a_lane;
+      const lds_u8* Bp = Bs + b_lane;
+      const lds_f32* Sp = Ss + s_lane;
+      auto aoff = [](int nb) {  // byte offset of weight block nb of this wave
+        return (nb < C::NB / 2 ? nb : 8 - C::NB / 2 + nb) * 2048;
       };
-      v8i aq = lds_frag(As, rblk(0), lane);
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) {
-        const v8i an = lds_frag(As, rblk(nb + 1 < C::NB ? nb + 1 : nb), lane);
+      if constexpr (C::NB > C::TBW) {
+        // Hold the token fragments; weight fragments stream one block ahead.
+        // The scheduling barrier keeps the compiler from hoisting every
+        // block's LDS reads to the top (all of them live at once).
+        v8i bq[C::TBW];
+        float r0[C::TBW], r1[C::TBW];
 #pragma unroll
         for (int tb = 0; tb < C::TBW; ++tb) {
-          const v4f p = mfma_fp8(aq, bq[tb]);
-          const float f = nb < C::NB / 2 ? f0[tb] : f1[tb];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[nb][tb][i] = fmaf(p[i], f, acc[nb][tb][i]);
+          bq[tb] = lds_frag(Bp + tb * 2048);
+          const float sx = Sp[tb * 16];
+          const float g0 = carry_scale(sx * sw0, fs0[tb]), g1 = carry_scale(sx * sw1, fs1[tb]);
+          r0[tb] = fs0[tb] * __builtin_amdgcn_rcpf(g0);
+          r1[tb] = fs1[tb] * __builtin_amdgcn_rcpf(g1);
+          fs0[tb] = g0;
+          fs1[tb] = g1;
         }
-        __builtin_amdgcn_sched_barrier(0);
-        aq = an;
+        v8i aq = lds_frag(Ap + aoff(0));
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) {
+          const v8i an = lds_frag(Ap + aoff(nb + 1 < C::NB ? nb + 1 : nb));
+#pragma unroll
+          for (int tb = 0; tb < C::TBW; ++tb) {
+            const float r = nb < C::NB / 2 ? r0[tb] : r1[tb];
+            acc[nb][tb] = mfma_fp8(aq, bq[tb], acc[nb][tb] * r);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          aq = an;
+        }
+      } else {
+        // Hold the weight fragments; token fragments stream one block ahead.
+        v8i aq[C::NB];
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) aq[nb] = lds_frag(Ap + aoff(nb));
+        v8i bq = lds_frag(Bp);
+        float sx = Sp[0];
+#pragma unroll
+        for (int tb = 0; tb < C::TBW; ++tb) {
+          const int tn = tb + 1 < C::TBW ? tb + 1 : tb;
+          const v8i bn = lds_frag(Bp + tn * 2048);
+          const float sn = Sp[tn * 16];
+          const float g0 = carry_scale(sx * sw0, fs0[tb]), g1 = carry_scale(sx * sw1, fs1[tb]);
+          const float r0 = fs0[tb] * __builtin_amdgcn_rcpf(g0), r1 = fs1[tb] * __builtin_amdgcn_rcpf(g1);
+          fs0[tb] = g0;
+          fs1[tb] = g1;
+#pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb) acc[nb][tb] = mfma_fp8(aq[nb], bq, acc[nb][tb] * (nb < C::NB / 2 ? r0 : r1));
+          __builtin_amdgcn_sched_barrier(0);
+          bq = bn;
+          sx = sn;
+        }
       }
     };
     issue(std::integral_constant<int, 0>{}, 0);
@@ -292,6 +340,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
       if (C::STAGES > 2 && kb + 2 < kbs) step(std::integral_constant<int, (C::STAGES > 2 ? 2 : 0)>{}, kb + 2);
       if (C::STAGES > 3 && kb + 3 < kbs) step(std::integral_constant<int, (C::STAGES > 3 ? 3 : 0)>{}, kb + 3);
     }
+    // undo the running scale: acc = sum_kb F_kb * (block product)
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int tb = 0; tb < C::TBW; ++tb) acc[nb][tb] *= (nb < C::NB / 2 ? fs0[tb] : fs1[tb]);
     __syncthreads();  // every wave is done with the ring before the epilogue reuses LDS
 
     // ---- epilogue -----------------------------------------------------------
@@ -374,6 +427,7 @@ static int launch_bt(const GemmArgs& a, int block_m, void* stream) {
     case 32: return launch_one<32, FC1>(a, stream);
     case 64: return launch_one<64, FC1>(a, stream);
     case 128: return launch_one<128, FC1>(a, stream);
+    case 256: return launch_one<256, FC1>(a, stream);
   }
   return -1;
 }
@@ -394,7 +448,8 @@ int gemm_max_workgroups_per_cu(int which, int block_m) {
     case 16: return f1 ? occ<16, true>() : occ<16, false>();
     case 32: return f1 ? occ<32, true>() : occ<32, false>();
     case 64: return f1 ? occ<64, true>() : occ<64, false>();
-    default: return f1 ? occ<128, true>() : occ<128, false>();
+    case 128: return f1 ? occ<128, true>() : occ<128, false>();
+    default: return f1 ? occ<256, true>() : occ<256, false>();
   }
 }
 

@@ -74,7 +74,7 @@ moe_status_t validate_config(const moe_config_t* cfg, int32_t expected_m, int32_
 }
 
 // Tile tactic from the expected rows per expert: the token tile (block_m)
-// is the token bucket, clamped to [16, 128].  Weights always come in 256-row
+// is the token bucket, clamped to [16, 256].  Weights always come in 256-row
 // tiles (FC1: 128 gate + 128 up rows of one 128-wide block of h; FC2: two
 // 128-row blocks of H).
 Tactic choose_tactic(const moe_config_t& cfg, int32_t expected_m) {
@@ -82,8 +82,8 @@ Tactic choose_tactic(const moe_config_t& cfg, int32_t expected_m) {
   Tactic t;
   t.bucket = token_bucket(expected_m);
   t.block_n = 256;
-  t.block_m = t.bucket <= 16 ? 16 : (t.bucket >= 128 ? 128 : t.bucket);
-  t.stages = t.block_m == 64 ? 3 : (t.block_m == 128 ? 3 : 4);
+  t.block_m = t.bucket <= 16 ? 16 : (t.bucket >= 256 ? 256 : t.bucket);
+  t.stages = t.block_m >= 256 ? 2 : (t.block_m >= 64 ? 3 : 4);
   return t;
 }
 
