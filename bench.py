@@ -27,6 +27,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+METRIC = "MoE layer TFLOP/s + % FP8 MFMA peak (HBM GB/s small T), 32 experts, T=8..32768"
 FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (no sparsity)
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
 
@@ -48,6 +49,41 @@ def workload_bytes(shape, counts, tokens, with_stage=True):
     meta = R * 16
     stage = (2 * tokens * H + tokens * H + tokens * H // 32) if with_stage else 0
     return w + x + h + y + out + meta + stage
+
+
+# HBM bytes per FC1 launch from the committed FETCH_SIZE / WRITE_SIZE counter
+# passes.  The figure is valid only for the kernel source it was taken on: the
+# file records a hash of the sources that decide the FC1 kernel and its launch.
+COUNTER_FILE = os.path.join(ROOT, "profiles", "fc1_dsv3_T4096_hbm_counters.txt")
+COUNTER_SOURCES = ["mixture_experts_ffn_route_amd/csrc/moe_gemm_fp8.hip",
+                   "mixture_experts_ffn_route_amd/csrc/moe_host.cpp",
+                   "mixture_experts_ffn_route_amd/csrc/moe_api.cpp"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in COUNTER_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload):
+    """FC1 HBM bytes per launch from the counter file, or None when absent,
+    taken on another workload, or taken on a different kernel source."""
+    try:
+        with open(COUNTER_FILE) as f:
+            kv = dict(ln.split(":", 1) for ln in f.read().splitlines() if ":" in ln and not ln.startswith(" "))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("source_hash") != kernel_source_hash() or kv.get("workload") != workload:
+        return None
+    try:
+        return int(kv["fc1_hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def fc1_flops(R, H, I):
@@ -180,8 +216,9 @@ def main():
         cpu = run_cpu_baseline(inp, min(args.cpu_sample, T))
         log(f"[bench] cpu baseline {cpu}")
 
+    workload = (f"{args.config} T={T} H={H} I={I} E={shape.experts} K={shape.top_k} routing={shape.routing}")
     line = {
-        "metric": "MoE layer TFLOP/s + % FP8 MFMA peak (HBM GB/s small T), 32 experts",
+        "metric": METRIC,
         "value": round(flops / sec / 1e12, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -193,14 +230,14 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8_e4m3",
         "data": "synthetic",
-        "config": {"workload": f"{args.config} T={T} H={H} I={I} E={shape.experts} K={shape.top_k} "
-                               f"routing={shape.routing}", "tokens": T, "routes": R,
+        "config": {"workload": workload, "tokens": T, "routes": R,
                    "hbm_gbs_algorithmic": round(B / sec / 1e9, 1),
                    "pct_fp8_peak": round(100 * flops / sec / 1e12 / FP8_PEAK_TFLOPS, 2),
                    "kernel_avg_ms": kern},
         "roofline": {"bound": "mfma", "kernel": "fc1 (FP8 grouped GEMM + SwiGLU + 1x128 requant)",
                      "achieved": round(achieved, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": stored_traffic(workload),
+                     "kernel_source_hash": kernel_source_hash()},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
