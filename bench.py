@@ -36,18 +36,25 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def workload_bytes(shape, counts, tokens, with_stage=True):
-    """Algorithmic HBM bytes of one step (see the design notes for each term)."""
+def workload_bytes(shape, counts, tokens, with_stage=True, mx=False):
+    """Algorithmic HBM bytes of one step (see the design notes for each term).
+    mx: MXFP8 weights (one E8M0 byte per 32) x BF16 activations carried as
+    two e4m3 terms plus one exponent word per 32 columns."""
     H, I = shape.hidden, shape.intermediate
     R = int(sum(counts))
     touched = int(sum(1 for c in counts if c > 0))
-    w = touched * (2 * I * H + H * I + 4 * ((2 * I // 128) * (H // 128) + (H // 128) * (I // 128)))
-    x = tokens * H + tokens * H // 32               # e4m3 rows + scales read by FC1
-    h = 2 * R * I * (1 + 4 / 128)                   # e4m3 h + scales, write + read
+    if mx:
+        w = touched * (2 * I * H + H * I) * (1 + 1 / 32)
+        row = lambda n: 2 * n + n // 8                 # noqa: E731  two term planes + exponent words
+    else:
+        w = touched * (2 * I * H + H * I + 4 * ((2 * I // 128) * (H // 128) + (H // 128) * (I // 128)))
+        row = lambda n: n + n // 32                    # noqa: E731  e4m3 row + 1x128 float32 scales
+    x = tokens * row(H)                             # activation rows read by FC1
+    h = 2 * R * row(I)                              # FC1 output rows, write + read
     y = 2 * R * H * 2                               # bf16 y, write + read
     out = tokens * H * 2
     meta = R * 16
-    stage = (2 * tokens * H + tokens * H + tokens * H // 32) if with_stage else 0
+    stage = (2 * tokens * H + tokens * row(H)) if with_stage else 0
     return w + x + h + y + out + meta + stage
 
 
@@ -100,9 +107,9 @@ def run_cpu_baseline(inp, sample_tokens):
     from oracle import moe_ref
 
     S = sample_tokens
+    fwd = moe_ref.forward_mx if inp.weight_format == "mxfp8" else moe_ref.forward_fp8
     t0 = time.perf_counter()
-    moe_ref.forward_fp8(inp.x_bf16[:S], inp.topk_idx[:S], inp.topk_w[:S], inp.w13, inp.w13_scale, inp.w2,
-                        inp.w2_scale)
+    fwd(inp.x_bf16[:S], inp.topk_idx[:S], inp.topk_w[:S], inp.w13, inp.w13_scale, inp.w2, inp.w2_scale)
     dt = time.perf_counter() - t0
     R = S * inp.shape.top_k
     flops = 6.0 * R * inp.shape.hidden * inp.shape.intermediate
@@ -120,6 +127,9 @@ def main():
     ap.add_argument("--config", default="dsv3", choices=["tiny", "small", "dsv3", "skewed"])
     ap.add_argument("--tokens", type=int, default=None, help="override T (token sweep)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--weights", default="fp8_block", choices=["fp8_block", "mxfp8"],
+                    help="fp8_block: e4m3 + 128x128 scales, e4m3 1x128 activations; "
+                         "mxfp8: e4m3 + E8M0 per 32 weights x BF16 activations")
     ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens for the CPU oracle baseline (0: skip)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (reference for HBM byte counters)")
@@ -140,14 +150,18 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     base = CONFIGS[args.config]
+    mx = args.weights == "mxfp8"
+    # The MXFP8 x BF16 path issues two FP8 MFMAs per K-block (hi and lo
+    # activation terms), so its ceiling in layer FLOPs is half the FP8 peak.
+    peak = FP8_PEAK_TFLOPS / 2 if mx else FP8_PEAK_TFLOPS
 
     def measure(tokens, steps, warmup):
         shape = MoEShape(tokens, base.hidden, base.intermediate, base.experts, base.top_k, base.routing)
         t0 = time.perf_counter()
-        inp = make_layer_inputs(shape, seed=args.seed)
+        inp = make_layer_inputs(shape, seed=args.seed, weight_format=args.weights)
         log(f"[bench] generated T={tokens} inputs in {time.perf_counter() - t0:.1f}s")
         dev = to_device(inp)
-        layer = make_layer(shape, dev)
+        layer = make_layer(shape, dev, mx=mx)
         out = torch.empty((tokens, shape.hidden), dtype=torch.bfloat16, device="cuda")
 
         def step():
@@ -174,10 +188,10 @@ def main():
         shape, _, layer, sec, prof, status, counts = measure(T, max(5, args.steps // 2), args.warmup)
         R = int(counts.sum())
         flops = 6.0 * R * shape.hidden * shape.intermediate
-        B = workload_bytes(shape, counts, T)
+        B = workload_bytes(shape, counts, T, mx=mx)
         kern = {k: v[0] / max(v[1], 1) for k, v in prof.items()}
         rec = {"tokens": T, "ms_per_step": sec * 1e3, "tflops": flops / sec / 1e12, "gbs": B / sec / 1e9,
-               "pct_fp8_peak": 100 * flops / sec / 1e12 / FP8_PEAK_TFLOPS, "pct_hbm_peak": 100 * B / sec / 1e9 / HBM_PEAK_GBS,
+               "pct_mfma_peak": 100 * flops / sec / 1e12 / peak, "weights": args.weights, "pct_hbm_peak": 100 * B / sec / 1e9 / HBM_PEAK_GBS,
                "kernel_ms": kern, "tactic": layer.tactic(), "status": status}
         log("[sweep]", json.dumps(rec))
         os.makedirs(os.path.dirname(args.sweep_out) or ".", exist_ok=True)
@@ -202,7 +216,7 @@ def main():
     R = int(counts.sum())
     H, I = shape.hidden, shape.intermediate
     flops = 6.0 * R * H * I
-    B = workload_bytes(shape, counts, T)
+    B = workload_bytes(shape, counts, T, mx=mx)
     fc1_ms, fc1_n = prof["fc1"]
     fc1_avg_s = fc1_ms / max(fc1_n, 1) / 1e3
     achieved = fc1_flops(R, H, I) / fc1_avg_s / 1e12
@@ -216,7 +230,8 @@ def main():
         cpu = run_cpu_baseline(inp, min(args.cpu_sample, T))
         log(f"[bench] cpu baseline {cpu}")
 
-    workload = (f"{args.config} T={T} H={H} I={I} E={shape.experts} K={shape.top_k} routing={shape.routing}")
+    workload = (f"{args.config} T={T} H={H} I={I} E={shape.experts} K={shape.top_k} routing={shape.routing}"
+                + (" weights=mxfp8 activations=bf16" if mx else ""))
     line = {
         "metric": METRIC,
         "value": round(flops / sec / 1e12, 3),
@@ -228,15 +243,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3",
+        "dtype": "bf16 x mxfp8_e4m3" if mx else "fp8_e4m3",
         "data": "synthetic",
         "config": {"workload": workload, "tokens": T, "routes": R,
                    "hbm_gbs_algorithmic": round(B / sec / 1e9, 1),
-                   "pct_fp8_peak": round(100 * flops / sec / 1e12 / FP8_PEAK_TFLOPS, 2),
+                   "pct_mfma_peak": round(100 * flops / sec / 1e12 / peak, 2),
                    "kernel_avg_ms": kern},
-        "roofline": {"bound": "mfma", "kernel": "fc1 (FP8 grouped GEMM + SwiGLU + 1x128 requant)",
-                     "achieved": round(achieved, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": stored_traffic(workload),
+        "roofline": {"bound": "mfma",
+                     "kernel": ("fc1 (MX-scaled FP8 grouped GEMM, two activation terms + SwiGLU + bf16 split)" if mx
+                                else "fc1 (FP8 grouped GEMM + SwiGLU + 1x128 requant)"),
+                     "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": stored_traffic(workload),
                      "kernel_source_hash": kernel_source_hash()},
         "cpu_baseline": cpu,
     }

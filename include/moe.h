@@ -64,7 +64,13 @@ enum {
 /* Activation formats (what moe_stage_inputs receives and FC1 consumes). */
 enum {
   MOE_ACT_E4M3_1X128 = 0,  /* e4m3 rows with one float32 scale per 128 columns */
-  MOE_ACT_BF16 = 1         /* bfloat16 rows, used as exact values (MXFP8 variant) */
+  /* bfloat16 rows (MXFP8 variant).  The gfx950 scaled MFMA takes FP8/FP6/FP4
+   * operands only, so each row is carried as two e4m3 terms with their own
+   * E8M0 exponent per 32 columns, hi = e4m3(x/2^a) and lo = e4m3((x - hi)/2^b);
+   * hi + lo keeps 8 significant bits, within 2^-9 of x relatively.  h between
+   * the GEMMs is rounded to bfloat16 (PR #4604, Description) and split the
+   * same way. */
+  MOE_ACT_BF16 = 1
 };
 
 /* cfg->flags */
@@ -128,18 +134,20 @@ enum {
   MOE_REGION_STATUS = 0,        /* uint32 [8]: status bits, staged tokens, kept routes, m-tiles */
   MOE_REGION_STAGED_IDX = 1,    /* int32 [max_rows*K]   expert per route, -1 masked */
   MOE_REGION_STAGED_W = 2,      /* float32 [max_rows*K] weight per route, 0 masked */
-  MOE_REGION_XQ = 3,            /* e4m3 [rows_x, H]  (bf16 [rows_x, H] for MOE_ACT_BF16) */
-  MOE_REGION_XS = 4,            /* float32 [rows_x, H/128] (unused for MOE_ACT_BF16) */
+  MOE_REGION_XQ = 3,            /* e4m3 [rows_x, H]; MOE_ACT_BF16: [2][rows_x, H] hi-term then lo-term codes */
+  MOE_REGION_XS = 4,            /* float32 [rows_x, H/128]; MOE_ACT_BF16: uint32 [rows_x, H/32] E8M0 pairs */
   MOE_REGION_COUNTS = 5,        /* int32 [E]   kept routes per expert */
   MOE_REGION_OFFSETS = 6,       /* int32 [E+1] exclusive prefix of counts */
   MOE_REGION_SORTED_ROUTE = 7,  /* int32 [row_cap] route ids t*K+k, expert-major, ascending in expert */
   MOE_REGION_ROUTE_POS = 8,     /* int32 [max_rows*K] inverse of sorted_route, -1 if not kept */
-  MOE_REGION_HQ = 9,            /* FC1 output rows [row_cap, I]: e4m3 (bf16 for MXFP8) */
-  MOE_REGION_HS = 10,           /* float32 [row_cap, I/128] (FP8 path) */
+  MOE_REGION_HQ = 9,            /* FC1 output rows: e4m3 [row_cap, I]; MXFP8: [2][row_cap, I] hi/lo-term codes */
+  MOE_REGION_HS = 10,           /* float32 [row_cap, I/128]; MXFP8: uint32 [row_cap, I/32] E8M0 pairs */
   MOE_REGION_Y = 11,            /* bf16 [row_cap, H] un-weighted FC2 rows */
   MOE_REGION_TILES = 12,        /* int32 [max_m_tiles, 2] (expert, first sorted row) */
   MOE_REGION_W13T = 13,         /* e4m3 w13 tiled at create: [E, I/128, H/128] tiles of 32 KB */
-  MOE_REGION_W2T = 14           /* e4m3 w2 tiled at create: [E, ceil(H/256), I/128] tiles of 32 KB */
+  MOE_REGION_W2T = 14,          /* e4m3 w2 tiled at create: [E, ceil(H/256), I/128] tiles of 32 KB */
+  MOE_REGION_W13S = 15,         /* MXFP8: w13 E8M0 tiled at create, 1 KB per w13 tile (empty for FP8) */
+  MOE_REGION_W2S = 16           /* MXFP8: w2 E8M0 tiled at create, 1 KB per w2 tile (empty for FP8) */
 };
 
 /* Kernel classes timed by the optional profiler. */
@@ -174,10 +182,12 @@ moe_status_t moe_workspace_query(const moe_config_t* cfg, int32_t expected_m, in
  *  stream          the weight transform is launched on it.
  *  out             [host out] new handle (host memory owned by the library).
  * Launches one transform per weight tensor that copies the e4m3 codes into
- * the workspace in the kernels' tile order (MOE_REGION_W13T / W2T); the
- * scale tensors are read in place.  The caller keeps the scale tensors alive
- * and unchanged while the handle exists; the e4m3 tensors may be released
- * once the stream has passed the create call. */
+ * the workspace in the kernels' tile order (MOE_REGION_W13T / W2T).
+ * E4M3_BLOCK128: the float32 scale tensors are read in place, so the caller
+ * keeps them alive and unchanged while the handle exists.  MXFP8_E4M3: the
+ * E8M0 tensors are tiled too (MOE_REGION_W13S / W2S).  Every tensor copied
+ * into the workspace may be released once the stream has passed the create
+ * call. */
 moe_status_t moe_layer_create(const moe_config_t* cfg, int32_t expected_m, int32_t max_rows,
                               float capacity_factor, const moe_weights_t* w, void* workspace,
                               size_t ws_bytes, void* stream, moe_layer_t** out);

@@ -38,6 +38,7 @@ MOE_DEV_CAPACITY = 8
 REGIONS = {
     "status": 0, "staged_idx": 1, "staged_w": 2, "xq": 3, "xs": 4, "counts": 5, "offsets": 6,
     "sorted_route": 7, "route_pos": 8, "hq": 9, "hs": 10, "y": 11, "tiles": 12, "w13t": 13, "w2t": 14,
+    "w13s": 15, "w2s": 16,
 }
 KERNELS = ("stage", "compact", "fc1", "fc2", "combine")
 

@@ -28,6 +28,7 @@ SOURCES = [
     "moe_stage.hip",
     "moe_compact.hip",
     "moe_gemm_fp8.hip",
+    "moe_gemm_mx.hip",
     "moe_combine.hip",
     "moe_weights.hip",
 ]

@@ -75,6 +75,22 @@ moe_status_t hip_fail(const char* what) {
   return moe::fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Weighted top-k combine of the FC2 rows into the bound output tensor.
+moe_status_t combine(moe_layer* l, int32_t T, hipStream_t s, void* stream) {
+  moe::CombineArgs cb;
+  cb.y = region<uint16_t>(l, MOE_REGION_Y);
+  cb.route_pos = region<int32_t>(l, MOE_REGION_ROUTE_POS);
+  cb.staged_w = region<float>(l, MOE_REGION_STAGED_W);
+  cb.tokens = T;
+  cb.top_k = l->cfg.top_k;
+  cb.hidden = l->cfg.hidden;
+  cb.out = static_cast<uint16_t*>(l->out);
+  const int p = prof_begin(l, MOE_KERNEL_COMBINE, s);
+  if (moe::launch_combine(cb, stream) != 0) return hip_fail("combine launch");
+  prof_end(l, p, s);
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" moe_status_t moe_layer_create(const moe_config_t* cfg, int32_t expected_m, int32_t max_rows,
@@ -93,8 +109,6 @@ extern "C" moe_status_t moe_layer_create(const moe_config_t* cfg, int32_t expect
     return moe::fail(MOE_ERR_INVALID_ARG, "weight scales must be 4-byte aligned");
   if (!workspace || ((uintptr_t)workspace & 255))
     return moe::fail(MOE_ERR_INVALID_ARG, "workspace must be non-NULL and 256-byte aligned");
-  if (cfg->weight_format != MOE_WEIGHT_E4M3_BLOCK128)
-    return moe::fail(MOE_ERR_UNSUPPORTED, "MXFP8 weights are not built into this library version");
   moe::Tactic t = moe::choose_tactic(*cfg, expected_m);
   moe::Layout L = moe::compute_layout(*cfg, t, max_rows, capacity_factor);
   if (ws_bytes < L.total)
@@ -116,8 +130,10 @@ extern "C" moe_status_t moe_layer_create(const moe_config_t* cfg, int32_t expect
   l->capacity_factor = capacity_factor;
   l->staged_tokens = -1;
   l->out = nullptr;
+  const bool mx = cfg->weight_format == MOE_WEIGHT_MXFP8_E4M3;
   auto grid = [&](int which) {
-    int g = cus * moe::gemm_max_workgroups_per_cu(which, t.block_m);
+    int g = cus * (mx ? moe::gemm_mx_max_workgroups_per_cu(which, t.block_m)
+                      : moe::gemm_max_workgroups_per_cu(which, t.block_m));
     g = (g / 8) * 8;
     return g < 8 ? 8 : g;
   };
@@ -126,10 +142,19 @@ extern "C" moe_status_t moe_layer_create(const moe_config_t* cfg, int32_t expect
   // weight codes -> kernel tile order, stream-ordered before any forward
   uint8_t* w13t = l->ws + L.off[MOE_REGION_W13T];
   uint8_t* w2t = l->ws + L.off[MOE_REGION_W2T];
-  if (moe::launch_tile_weights(static_cast<const uint8_t*>(w->w13), w13t, cfg->num_experts, 2 * cfg->intermediate,
-                               cfg->hidden, cfg->intermediate / 128, cfg->intermediate, true, stream) != 0 ||
-      moe::launch_tile_weights(static_cast<const uint8_t*>(w->w2), w2t, cfg->num_experts, cfg->hidden,
-                               cfg->intermediate, (cfg->hidden + 255) / 256, cfg->intermediate, false, stream) != 0) {
+  const int E = cfg->num_experts, H = cfg->hidden, I = cfg->intermediate;
+  bool ok = moe::launch_tile_weights(static_cast<const uint8_t*>(w->w13), w13t, E, 2 * I, H, I / 128, I, true, mx,
+                                     stream) == 0 &&
+            moe::launch_tile_weights(static_cast<const uint8_t*>(w->w2), w2t, E, H, I, (H + 255) / 256, I, false, mx,
+                                     stream) == 0;
+  if (ok && mx)
+    ok = moe::launch_tile_mx_scales(static_cast<const uint8_t*>(w->w13_scale),
+                                    reinterpret_cast<uint32_t*>(l->ws + L.off[MOE_REGION_W13S]), E, 2 * I, H, I / 128,
+                                    I, true, stream) == 0 &&
+         moe::launch_tile_mx_scales(static_cast<const uint8_t*>(w->w2_scale),
+                                    reinterpret_cast<uint32_t*>(l->ws + L.off[MOE_REGION_W2S]), E, H, I,
+                                    (H + 255) / 256, I, false, stream) == 0;
+  if (!ok) {
     delete l;
     return hip_fail("weight transform launch");
   }
@@ -176,6 +201,8 @@ extern "C" moe_status_t moe_stage_inputs(moe_layer_t* l, const void* x, const fl
   a.staged_w = region<float>(l, MOE_REGION_STAGED_W);
   a.xq = region<uint8_t>(l, MOE_REGION_XQ);
   a.xs = region<float>(l, MOE_REGION_XS);
+  a.x_plane = (int64_t)l->L.rows_x * l->cfg.hidden;
+  a.xs_mx = region<uint32_t>(l, MOE_REGION_XS);
   const int p = prof_begin(l, MOE_KERNEL_STAGE, s);
   if (moe::launch_stage(a, stream) != 0) return hip_fail("stage launch");
   prof_end(l, p, s);
@@ -210,6 +237,57 @@ extern "C" moe_status_t moe_layer_forward(moe_layer_t* l, void* stream) {
   int p = prof_begin(l, MOE_KERNEL_COMPACT, s);
   if (moe::launch_compact(ca, stream) != 0) return hip_fail("compact launch");
   prof_end(l, p, s);
+
+  if (c.weight_format == MOE_WEIGHT_MXFP8_E4M3) {
+    moe::MxGemmArgs m1;
+    memset(&m1, 0, sizeof(m1));
+    m1.a = region<uint8_t>(l, MOE_REGION_XQ);
+    m1.a_plane = (int64_t)l->L.rows_x * c.hidden;
+    m1.a_scale = region<uint32_t>(l, MOE_REGION_XS);
+    m1.a_mode = 1;
+    m1.sorted_route = ca.sorted_route;
+    m1.top_k = c.top_k;
+    m1.w = region<uint8_t>(l, MOE_REGION_W13T);
+    m1.w_scale = region<uint32_t>(l, MOE_REGION_W13S);
+    m1.n_rows = 2 * c.intermediate;
+    m1.k_dim = c.hidden;
+    m1.inter = c.intermediate;
+    m1.n_tiles = c.intermediate / 128;
+    m1.tiles = ca.tiles;
+    m1.offsets = ca.offsets;
+    m1.hdr = ca.hdr;
+    m1.hq = region<uint8_t>(l, MOE_REGION_HQ);
+    m1.h_plane = l->L.row_cap * c.intermediate;
+    m1.hs = region<uint32_t>(l, MOE_REGION_HS);
+    m1.grid = l->grid_fc1;
+    p = prof_begin(l, MOE_KERNEL_FC1, s);
+    if (moe::launch_fc1_mx(m1, l->tac.block_m, stream) != 0) return hip_fail("fc1 launch");
+    prof_end(l, p, s);
+
+    moe::MxGemmArgs m2;
+    memset(&m2, 0, sizeof(m2));
+    m2.a = m1.hq;
+    m2.a_plane = m1.h_plane;
+    m2.a_scale = m1.hs;
+    m2.a_mode = 0;
+    m2.sorted_route = ca.sorted_route;
+    m2.top_k = c.top_k;
+    m2.w = region<uint8_t>(l, MOE_REGION_W2T);
+    m2.w_scale = region<uint32_t>(l, MOE_REGION_W2S);
+    m2.n_rows = c.hidden;
+    m2.k_dim = c.intermediate;
+    m2.inter = c.intermediate;
+    m2.n_tiles = (c.hidden + 255) / 256;
+    m2.tiles = ca.tiles;
+    m2.offsets = ca.offsets;
+    m2.hdr = ca.hdr;
+    m2.y = region<uint16_t>(l, MOE_REGION_Y);
+    m2.grid = l->grid_fc2;
+    p = prof_begin(l, MOE_KERNEL_FC2, s);
+    if (moe::launch_fc2_mx(m2, l->tac.block_m, stream) != 0) return hip_fail("fc2 launch");
+    prof_end(l, p, s);
+    return combine(l, T, s, stream);
+  }
 
   moe::GemmArgs g1;
   memset(&g1, 0, sizeof(g1));
@@ -256,18 +334,7 @@ extern "C" moe_status_t moe_layer_forward(moe_layer_t* l, void* stream) {
   if (moe::launch_fc2(g2, l->tac.block_m, stream) != 0) return hip_fail("fc2 launch");
   prof_end(l, p, s);
 
-  moe::CombineArgs cb;
-  cb.y = g2.y;
-  cb.route_pos = ca.route_pos;
-  cb.staged_w = region<float>(l, MOE_REGION_STAGED_W);
-  cb.tokens = T;
-  cb.top_k = c.top_k;
-  cb.hidden = c.hidden;
-  cb.out = static_cast<uint16_t*>(l->out);
-  p = prof_begin(l, MOE_KERNEL_COMBINE, s);
-  if (moe::launch_combine(cb, stream) != 0) return hip_fail("combine launch");
-  prof_end(l, p, s);
-  return MOE_OK;
+  return combine(l, T, s, stream);
 }
 
 extern "C" moe_status_t moe_read_status(moe_layer_t* l, void* stream, uint32_t* bits) {
@@ -285,7 +352,7 @@ extern "C" moe_status_t moe_read_status(moe_layer_t* l, void* stream, uint32_t* 
 extern "C" moe_status_t moe_layer_region(moe_layer_t* l, int32_t r, void** dptr, size_t* bytes) {
   moe::clear_error();
   if (!l || !dptr || !bytes) return moe::fail(MOE_ERR_INVALID_ARG, "NULL argument");
-  if (r < 0 || r > MOE_REGION_W2T) return moe::fail(MOE_ERR_INVALID_ARG, "unknown region %d", r);
+  if (r < 0 || r > MOE_REGION_W2S) return moe::fail(MOE_ERR_INVALID_ARG, "unknown region %d", r);
   *dptr = l->ws + l->L.off[r];
   *bytes = l->L.size[r];
   return MOE_OK;

@@ -30,6 +30,36 @@ __device__ __forceinline__ int cvt2_e4m3(float a, float b, int old, bool hi) {
             : __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, false);
 }
 
+// e4m3 code (OCP E4M3FN, finite) -> float, from its bit fields:
+// exponent field 0 is subnormal m/8 * 2^-6, otherwise (1 + m/8) * 2^(e-7).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const int m = (int)(c & 7u), e = (int)((c >> 3) & 15u);
+  const float mag = e ? ldexpf((float)(8 + m), e - 10) : ldexpf((float)m, -9);
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// E8M0 exponent of one 32-element block for the two-term split of BF16
+// values: the block maximum lands in [128, 256), so no e4m3 code of the
+// block saturates.  An all-zero block gets 2^0 (its codes are zero).
+__device__ __forceinline__ int mx_block_exp(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  const int e = __builtin_amdgcn_frexp_expf(amax) - 8;  // amax in [2^(x-1), 2^x) -> x - 8
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Four values of one block -> four e4m3 codes of v / 2^e (packed, code i in
+// byte i), and the residuals v - code_i * 2^e, which are exact in float for
+// BF16 inputs.
+__device__ __forceinline__ uint32_t mx_term4(const float v[4], int e, float r[4]) {
+  const int neg = -e;
+  int w = cvt2_e4m3(ldexpf(v[0], neg), ldexpf(v[1], neg), 0, false);
+  w = cvt2_e4m3(ldexpf(v[2], neg), ldexpf(v[3], neg), w, true);
+  const uint32_t u = (uint32_t)w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = v[i] - ldexpf(e4m3_to_f32((u >> (8 * i)) & 0xffu), e);
+  return u;
+}
+
 // Maximum over groups of `width` consecutive lanes (width a power of two <= 64).
 template <int WIDTH>
 __device__ __forceinline__ float group_max(float v) {

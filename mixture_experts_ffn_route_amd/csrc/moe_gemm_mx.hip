@@ -1,0 +1,395 @@
+// MXFP8-weight x BF16-activation grouped GEMMs of the MoE layer on gfx950
+// MX-scaled MFMA (the variant of "feat(moe_ep): MXFP8 x BF16 integration",
+// flashinfer PR #4604, Description: e4m3 weights with one E8M0 exponent per
+// 32 K-elements, BF16 activations, BF16 h between the GEMMs).
+//
+// FC1: gu[p, n] = sum_k x[t, k] * w13[e, n, k] * 2^(s13[e, n, k/32] - 127)
+//      h = bf16_RNE(silu(gate) * up)
+// FC2: y[p, n]  = sum_k h[p, k] * w2[e, n, k] * 2^(s2[e, n, k/32] - 127)  -> bf16
+//
+// The scaled f8f6f4 MFMA takes FP8/FP6/FP4 operands only, so every BF16
+// activation row is carried as two e4m3 terms with their own E8M0 exponent
+// per 32 elements, hi = e4m3(x / 2^e_hi) and lo = e4m3((x - hi) / 2^e_lo)
+// (made by the stage kernel for x and by the FC1 epilogue for h).  A K-block
+// is then two scaled MFMAs into one FP32 accumulator; the hardware applies
+// both the weight and the activation exponents, so no per-block VALU work
+// remains.  hi + lo keeps 8 significant bits of each BF16 value; the
+// remaining error is below 2^-9 relative per element.
+//
+// Structure as the FP8 kernel (moe_gemm_fp8.hip): swap-AB (weights are the
+// MFMA row operand), 256 weight rows x BT tokens per workgroup tile, 8 waves,
+// LDS-DMA ring with explicit waits, fragment-ordered LDS, persistent
+// XCD-aware tile walk.  Per ring stage: 32 KB of weight codes, 1 KB of weight
+// exponents, 2 x BT x 128 bytes of activation terms and BT x 16 bytes of
+// activation exponents.
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 512;
+constexpr int kWaves = 8;
+constexpr int kBN = 256;
+constexpr int kKB = 128;
+constexpr int kGroupM = 4;
+constexpr int kLdsBytes = 160 * 1024;
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+
+// Scaled MFMA: A = weights (row operand), B = activation term (column
+// operand).  OA / OB pick the byte of the scale words: lane l's scale word
+// supplies the exponent of row (or column) l%16 for 32-block l/16.
+template <int OA, int OB>
+__device__ __forceinline__ v4f mfma_mx(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, OA, sa, OB, sb);
+}
+
+__device__ __forceinline__ v8i lds_frag(const lds_u8* p) {
+  const u32x4 lo = *reinterpret_cast<lds_u32x4*>(p);
+  const u32x4 hi = *reinterpret_cast<lds_u32x4*>(p + 1024);
+  v8i r;
+  r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];
+  r[4] = (int)hi[0]; r[5] = (int)hi[1]; r[6] = (int)hi[2]; r[7] = (int)hi[3];
+  return r;
+}
+
+// LDS-DMA, explicit waits and a fence-free barrier, as in the FP8 kernel.
+__device__ __forceinline__ uint32_t lds_addr(const lds_u8* p) { return (uint32_t)(uintptr_t)p; }
+__device__ __forceinline__ void dma16(const uint8_t* src, const lds_u8* lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const uint32_t* src, const lds_u8* lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+template <int BT>
+struct MxCfg {
+  static constexpr int WN = BT >= 64 ? 2 : (BT == 32 ? 4 : 8);  // waves along weight rows
+  static constexpr int WT = kWaves / WN;
+  static constexpr int G = 128 / WN;          // rows of each 128-row half per wave
+  static constexpr int NBH = G / 16;          // 16-row blocks per half per wave (1, 2 or 4)
+  static constexpr int NB = 2 * NBH;
+  static constexpr int TW = BT / WT;
+  static constexpr int TBW = TW / 16;
+  static constexpr int A_BYTES = kBN * kKB;   // weight codes
+  static constexpr int AS_BYTES = 1024;       // weight exponents
+  static constexpr int B_BYTES = 2 * BT * kKB;  // hi and lo activation terms
+  static constexpr int BS_BYTES = ((BT * 16 + 255) / 256) * 256;  // activation exponent words
+  static constexpr int STAGE = A_BYTES + AS_BYTES + B_BYTES + BS_BYTES;
+  static constexpr int STAGES = (kLdsBytes / STAGE) > 4 ? 4 : (kLdsBytes / STAGE);
+  static constexpr int B_PIECES = 2 * BT;     // 16-byte activation pieces per wave per stage
+  static constexpr int B_INSTR = (B_PIECES + 63) / 64;
+  static constexpr int B_LANES = B_PIECES < 64 ? B_PIECES : 64;
+  static constexpr int BS_LANES = BT / 2;     // activation exponent words per wave per stage
+  static constexpr int N_LD = 4 + 1 + B_INSTR + 1;
+  static_assert(TBW >= 1 && NBH >= 1 && NBH <= 4 && STAGES >= 2, "tile shape");
+  static_assert(BS_LANES <= 64 && (STAGES - 2) * N_LD < 64, "load shape");
+  static_assert(2 * 8 * BT * 4 <= STAGE, "epilogue scratch fits in ring stage 0");
+};
+
+template <int BT, bool FC1>
+__global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
+  using C = MxCfg<BT>;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring2[C::STAGES > 2 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring3[C::STAGES > 3 ? C::STAGE : 16];
+  auto ring = [&](auto stage) -> lds_u8* {
+    constexpr int S = decltype(stage)::value;
+    if constexpr (S == 0) return (lds_u8*)ring0;
+    else if constexpr (S == 1) return (lds_u8*)ring1;
+    else if constexpr (S == 2) return (lds_u8*)ring2;
+    else return (lds_u8*)ring3;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave % C::WN, wt = wave / C::WN;
+  const int kbs = a.k_dim / kKB;
+  const int kq = a.k_dim / 32;
+  const int total_m = __builtin_amdgcn_readfirstlane((int)a.hdr[kHdrMTiles]);
+  const int64_t total = (int64_t)total_m * a.n_tiles;
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  const int per_xcd = gridDim.x >> 3;
+  const int64_t v_begin = total * xcd / 8, v_end = total * (xcd + 1) / 8;
+  const uint32_t a_lane = (uint32_t)(wn * C::NBH) * 2048u + (uint32_t)lane * 16u;
+  const uint32_t b_lane = (uint32_t)(wt * C::TBW) * 4096u + (uint32_t)lane * 16u;
+  const uint32_t bs_lane = (uint32_t)(wt * C::TBW * 64 + lane);
+  // weight exponents: word group of the wave's first gate/first-half block,
+  // and the byte of that block inside the word
+  const int sa_grp = (wn * C::NBH) / 4;
+  const int sa_shift = 8 * ((wn * C::NBH) % 4);
+
+  for (int64_t v = v_begin + slot; v < v_end; v += per_xcd) {
+    const int64_t group = v / ((int64_t)kGroupM * a.n_tiles);
+    const int64_t rem = v - group * kGroupM * a.n_tiles;
+    const int m0 = (int)(group * kGroupM);
+    const int gm = min(kGroupM, total_m - m0);
+    const int nt = (int)(rem / gm);
+    const int mt = m0 + (int)(rem % gm);
+    const int e = __builtin_amdgcn_readfirstlane(a.tiles[2 * mt]);
+    const int p0 = __builtin_amdgcn_readfirstlane(a.tiles[2 * mt + 1]);
+    const int rows_valid = min(BT, __builtin_amdgcn_readfirstlane(a.offsets[e + 1]) - p0);
+
+    const int64_t tile0 = ((int64_t)e * a.n_tiles + nt) * kbs;
+    const uint8_t* a_src = a.w + tile0 * C::A_BYTES + (wave * 4 * 64 + lane) * 16;
+    const uint32_t* as_src = a.w_scale + tile0 * 256 + wave * 32 + (lane < 32 ? lane : 0);
+    auto src_row = [&](int t) -> int64_t {
+      const int p = p0 + min(t, rows_valid - 1);
+      if (!FC1) return p;
+      const int r = a.sorted_route[p];
+      return r / a.top_k;
+    };
+    // activation terms: piece V of the wave covers LDS chunk V/64 = (token
+    // block, term, half); lane piece lp = (column group, token)
+    const uint8_t* b_src[C::B_INSTR];
+#pragma unroll
+    for (int j = 0; j < C::B_INSTR; ++j) {
+      const int pv = wave * C::B_PIECES + j * 64 + (lane < C::B_LANES ? lane : 0);
+      const int c = pv >> 6, lp = pv & 63;
+      const int t = (c >> 2) * 16 + (lp & 15);
+      const int term = (c >> 1) & 1, half = c & 1;
+      b_src[j] = a.a + term * a.a_plane + src_row(t) * a.k_dim + 64 * half + 16 * (lp >> 4);
+    }
+    // activation exponents: word U covers token block U/64, lane U%64 =
+    // token (U%16) and 32-block (U%64)/16
+    const uint32_t* bs_src;
+    {
+      const int u = wave * C::BS_LANES + (lane < C::BS_LANES ? lane : 0);
+      const int lp = u & 63;
+      bs_src = a.a_scale + src_row((u >> 6) * 16 + (lp & 15)) * kq + (lp >> 4);
+    }
+
+    auto issue = [&](auto stage, int kb) {
+      const lds_u8* As = ring(stage);
+      const lds_u8* ASs = As + C::A_BYTES;
+      const lds_u8* Bs = ASs + C::AS_BYTES;
+      const lds_u8* BSs = Bs + C::B_BYTES;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma16(a_src + (int64_t)kb * C::A_BYTES + j * 1024, As + (wave * 4 + j) * 1024);
+      if (lane < 32) dma4(as_src + kb * 256, ASs + wave * 128);
+#pragma unroll
+      for (int j = 0; j < C::B_INSTR; ++j)
+        if (lane < C::B_LANES) dma16(b_src[j] + kb * kKB, Bs + (wave * C::B_PIECES + j * 64) * 16);
+      if (lane < C::BS_LANES) dma4(bs_src + kb * 4, BSs + wave * C::BS_LANES * 4);
+    };
+
+    v4f acc[C::NB][C::TBW];
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int tb = 0; tb < C::TBW; ++tb) acc[nb][tb] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    auto step = [&](auto stage, int kb) {
+      constexpr int ST = decltype(stage)::value;
+      const int ahead = min(C::STAGES - 2, kbs - 1 - kb);
+      if (C::STAGES >= 4 && ahead >= 2) wait_vmcnt<(C::STAGES >= 4 ? 2 : 0) * C::N_LD>();
+      else if (C::STAGES >= 3 && ahead >= 1) wait_vmcnt<(C::STAGES >= 3 ? 1 : 0) * C::N_LD>();
+      else wait_vmcnt<0>();
+      barrier_nofence();
+      if (kb + C::STAGES - 1 < kbs)
+        issue(std::integral_constant<int, (ST + C::STAGES - 1) % C::STAGES>{}, kb + C::STAGES - 1);
+
+      const lds_u8* As = ring(stage);
+      const lds_u32* ASs = (const lds_u32*)(As + C::A_BYTES);
+      const lds_u8* Bs = As + C::A_BYTES + C::AS_BYTES;
+      const lds_u32* BSs = (const lds_u32*)(Bs + C::B_BYTES);
+      const lds_u8* Ap = As + a_lane;
+      const lds_u8* Bp = Bs + b_lane;
+      v8i bh[C::TBW], bl[C::TBW];
+      int sb[C::TBW];
+#pragma unroll
+      for (int tb = 0; tb < C::TBW; ++tb) {
+        bh[tb] = lds_frag(Bp + tb * 4096);
+        bl[tb] = lds_frag(Bp + tb * 4096 + 2048);
+        sb[tb] = (int)BSs[bs_lane + tb * 64];
+      }
+      const int sa_g = (int)(ASs[sa_grp * 64 + lane] >> sa_shift);
+      const int sa_u = (int)(ASs[(2 + sa_grp) * 64 + lane] >> sa_shift);
+      auto aoff = [](int nb) { return (nb < C::NBH ? nb : 8 - C::NBH + nb) * 2048; };
+      v8i aq = lds_frag(Ap + aoff(0));
+      static_for<0, C::NB>([&](auto nbc) {
+        constexpr int nb = decltype(nbc)::value;
+        constexpr int OA = nb % C::NBH;
+        const v8i an = lds_frag(Ap + aoff(nb + 1 < C::NB ? nb + 1 : nb));
+        const int sa = nb < C::NBH ? sa_g : sa_u;
+#pragma unroll
+        for (int tb = 0; tb < C::TBW; ++tb) {
+          acc[nb][tb] = mfma_mx<OA, 0>(aq, bh[tb], acc[nb][tb], sa, sb[tb]);
+          acc[nb][tb] = mfma_mx<OA, 1>(aq, bl[tb], acc[nb][tb], sa, sb[tb]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        aq = an;
+      });
+    };
+    issue(std::integral_constant<int, 0>{}, 0);
+    if (C::STAGES > 2 && 1 < kbs) issue(std::integral_constant<int, 1>{}, 1);
+    if (C::STAGES > 3 && 2 < kbs) issue(std::integral_constant<int, (C::STAGES > 3 ? 2 : 0)>{}, 2);
+    for (int kb = 0; kb < kbs; kb += C::STAGES) {
+      step(std::integral_constant<int, 0>{}, kb);
+      if (kb + 1 < kbs) step(std::integral_constant<int, 1>{}, kb + 1);
+      if (C::STAGES > 2 && kb + 2 < kbs) step(std::integral_constant<int, (C::STAGES > 2 ? 2 : 0)>{}, kb + 2);
+      if (C::STAGES > 3 && kb + 3 < kbs) step(std::integral_constant<int, (C::STAGES > 3 ? 3 : 0)>{}, kb + 3);
+    }
+    __syncthreads();  // every wave is done with the ring before the epilogue reuses LDS
+
+    if (FC1) {
+      // h = bf16(silu(g) * up), then the two-term split per 32 rows of h.
+      // A lane holds 4 consecutive rows of a 16-row block for one token; a
+      // 32-block is two row blocks, which may sit in different waves, so the
+      // block maxima go through LDS: red[rb][t] (pass 1: |h|, pass 2: |h - hi|).
+      float* red1 = reinterpret_cast<float*>(ring0);
+      float* red2 = red1 + 8 * BT;
+      const int iq = a.inter / 32;
+      float hv[C::TBW][C::NBH][4];
+#pragma unroll
+      for (int tb = 0; tb < C::TBW; ++tb)
+#pragma unroll
+        for (int g = 0; g < C::NBH; ++g) {
+          float m = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float gt = acc[g][tb][i], up = acc[C::NBH + g][tb][i];
+            const float h = bf16_to_f32(f32_to_bf16_rne(gt / (1.0f + expf(-gt)) * up));
+            hv[tb][g][i] = h;
+            m = fmaxf(m, fabsf(h));
+          }
+          m = fmaxf(m, __shfl_xor(m, 16));
+          m = fmaxf(m, __shfl_xor(m, 32));
+          if (lane < 16) red1[(wn * C::NBH + g) * BT + wt * C::TW + tb * 16 + lane] = m;
+        }
+      __syncthreads();
+      uint32_t hi_codes[C::TBW][C::NBH];
+      int ehi[C::TBW][C::NBH];
+#pragma unroll
+      for (int tb = 0; tb < C::TBW; ++tb)
+#pragma unroll
+        for (int g = 0; g < C::NBH; ++g) {
+          const int t = wt * C::TW + tb * 16 + (lane & 15);
+          const int rb = wn * C::NBH + g;
+          const int r0 = rb & ~1;
+          ehi[tb][g] = mx_block_exp(fmaxf(red1[r0 * BT + t], red1[(r0 + 1) * BT + t]));
+          float r[4];
+          hi_codes[tb][g] = mx_term4(hv[tb][g], ehi[tb][g], r);
+          float m = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            hv[tb][g][i] = r[i];
+            m = fmaxf(m, fabsf(r[i]));
+          }
+          m = fmaxf(m, __shfl_xor(m, 16));
+          m = fmaxf(m, __shfl_xor(m, 32));
+          if (lane < 16) red2[rb * BT + t] = m;
+        }
+      __syncthreads();
+#pragma unroll
+      for (int tb = 0; tb < C::TBW; ++tb)
+#pragma unroll
+        for (int g = 0; g < C::NBH; ++g) {
+          const int t = wt * C::TW + tb * 16 + (lane & 15);
+          const int rb = wn * C::NBH + g;
+          const int r0 = rb & ~1;
+          const int elo = mx_block_exp(fmaxf(red2[r0 * BT + t], red2[(r0 + 1) * BT + t]));
+          float unused[4];
+          const uint32_t lo_codes = mx_term4(hv[tb][g], elo, unused);
+          if (t < rows_valid) {
+            const int64_t off = (int64_t)(p0 + t) * a.inter + nt * 128 + rb * 16 + 4 * (lane >> 4);
+            *reinterpret_cast<uint32_t*>(a.hq + off) = hi_codes[tb][g];
+            *reinterpret_cast<uint32_t*>(a.hq + a.h_plane + off) = lo_codes;
+            if ((rb & 1) == 0 && (lane >> 4) == 0)
+              a.hs[(int64_t)(p0 + t) * iq + nt * 4 + rb / 2] =
+                  (uint32_t)(ehi[tb][g] + 127) | ((uint32_t)(elo + 127) << 8);
+          }
+        }
+    } else {
+      const int n0 = nt * kBN;
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) {
+        const int n = (nb < C::NBH ? wn * C::G + nb * 16 : 128 + wn * C::G + (nb - C::NBH) * 16) + 4 * (lane >> 4);
+#pragma unroll
+        for (int tb = 0; tb < C::TBW; ++tb) {
+          const int t = wt * C::TW + tb * 16 + (lane & 15);
+          if (t < rows_valid && n0 + n < a.n_rows) {
+            u32x2 o;
+            o[0] = f32_to_bf16_rne(acc[nb][tb][0]) | (f32_to_bf16_rne(acc[nb][tb][1]) << 16);
+            o[1] = f32_to_bf16_rne(acc[nb][tb][2]) | (f32_to_bf16_rne(acc[nb][tb][3]) << 16);
+            *reinterpret_cast<u32x2*>(a.y + (int64_t)(p0 + t) * a.n_rows + n0 + n) = o;
+          }
+        }
+      }
+    }
+    __syncthreads();  // the next tile's DMA reuses the LDS the epilogue read
+  }
+}
+
+template <int BT, bool FC1>
+int launch_one(const MxGemmArgs& a, void* stream) {
+  hipLaunchKernelGGL((gemm_mx_kernel<BT, FC1>), dim3(a.grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                     a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+template <bool FC1>
+int launch_bt(const MxGemmArgs& a, int block_m, void* stream) {
+  switch (block_m) {
+    case 16: return launch_one<16, FC1>(a, stream);
+    case 32: return launch_one<32, FC1>(a, stream);
+    case 64: return launch_one<64, FC1>(a, stream);
+    case 128: return launch_one<128, FC1>(a, stream);
+  }
+  return -1;
+}
+
+template <int BT, bool FC1>
+int occ() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_mx_kernel<BT, FC1>, kThreads, 0) != hipSuccess) return 1;
+  return n > 0 ? n : 1;
+}
+
+}  // namespace
+
+int launch_fc1_mx(const MxGemmArgs& a, int block_m, void* stream) { return launch_bt<true>(a, block_m, stream); }
+int launch_fc2_mx(const MxGemmArgs& a, int block_m, void* stream) { return launch_bt<false>(a, block_m, stream); }
+
+int gemm_mx_max_workgroups_per_cu(int which, int block_m) {
+  const bool f1 = which == 1;
+  switch (block_m) {
+    case 16: return f1 ? occ<16, true>() : occ<16, false>();
+    case 32: return f1 ? occ<32, true>() : occ<32, false>();
+    case 64: return f1 ? occ<64, true>() : occ<64, false>();
+    default: return f1 ? occ<128, true>() : occ<128, false>();
+  }
+}
+
+}  // namespace moe

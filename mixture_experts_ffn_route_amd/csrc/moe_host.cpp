@@ -77,13 +77,16 @@ moe_status_t validate_config(const moe_config_t* cfg, int32_t expected_m, int32_
 // is the token bucket, clamped to [16, 256].  Weights always come in 256-row
 // tiles (FC1: 128 gate + 128 up rows of one 128-wide block of h; FC2: two
 // 128-row blocks of H).
+// The MXFP8 variant stages two activation terms per K-block, so its token
+// tile stops at 128 (two ring stages of 67 KB).
 Tactic choose_tactic(const moe_config_t& cfg, int32_t expected_m) {
-  (void)cfg;
   Tactic t;
   t.bucket = token_bucket(expected_m);
   t.block_n = 256;
-  t.block_m = t.bucket <= 16 ? 16 : (t.bucket >= 256 ? 256 : t.bucket);
+  const int cap = cfg.weight_format == MOE_WEIGHT_MXFP8_E4M3 ? 128 : 256;
+  t.block_m = t.bucket <= 16 ? 16 : (t.bucket >= cap ? cap : t.bucket);
   t.stages = t.block_m >= 256 ? 2 : (t.block_m >= 64 ? 3 : 4);
+  if (cfg.weight_format == MOE_WEIGHT_MXFP8_E4M3) t.stages = t.block_m >= 128 ? 2 : (t.block_m >= 32 ? 3 : 4);
   return t;
 }
 
@@ -93,7 +96,7 @@ Layout compute_layout(const moe_config_t& cfg, const Tactic& t, int32_t max_rows
   Layout L;
   memset(&L, 0, sizeof(L));
   const int64_t K = cfg.top_k, H = cfg.hidden, I = cfg.intermediate, E = cfg.num_experts;
-  const bool bf16_act = cfg.act_format == MOE_ACT_BF16;
+  const bool mx = cfg.act_format == MOE_ACT_BF16;  // MXFP8 weights x BF16 activations
   L.route_slots = (int64_t)max_rows * K;
   L.rows_x = (cfg.flags & MOE_FLAG_PER_ROUTE_STAGING) ? L.route_slots : max_rows;
   double cap = ceil((double)capacity_factor * (double)L.route_slots);
@@ -105,19 +108,22 @@ Layout compute_layout(const moe_config_t& cfg, const Tactic& t, int32_t max_rows
   L.size[MOE_REGION_STATUS] = 256;
   L.size[MOE_REGION_STAGED_IDX] = L.route_slots * 4;
   L.size[MOE_REGION_STAGED_W] = L.route_slots * 4;
-  L.size[MOE_REGION_XQ] = L.rows_x * H * (bf16_act ? 2 : 1);
-  L.size[MOE_REGION_XS] = bf16_act ? 0 : L.rows_x * (H / 128) * 4;
+  L.size[MOE_REGION_XQ] = L.rows_x * H * (mx ? 2 : 1);  // MX: hi-term and lo-term planes
+  L.size[MOE_REGION_XS] = mx ? L.rows_x * (H / 32) * 4 : L.rows_x * (H / 128) * 4;
   L.size[MOE_REGION_COUNTS] = E * 4;
   L.size[MOE_REGION_OFFSETS] = (E + 1) * 4;
   L.size[MOE_REGION_SORTED_ROUTE] = L.row_cap * 4;
   L.size[MOE_REGION_ROUTE_POS] = L.route_slots * 4;
-  L.size[MOE_REGION_HQ] = L.row_cap * I * (bf16_act ? 2 : 1);
-  L.size[MOE_REGION_HS] = bf16_act ? 0 : L.row_cap * (I / 128) * 4;
+  L.size[MOE_REGION_HQ] = L.row_cap * I * (mx ? 2 : 1);
+  L.size[MOE_REGION_HS] = mx ? L.row_cap * (I / 32) * 4 : L.row_cap * (I / 128) * 4;
   L.size[MOE_REGION_Y] = L.row_cap * H * 2;
   L.size[MOE_REGION_TILES] = L.max_m_tiles * 2 * 4;
   // create-time tiled copies of the e4m3 weights (FC2 padded to 256-row tiles)
   L.size[MOE_REGION_W13T] = E * (2 * I) * H;
   L.size[MOE_REGION_W2T] = E * ((H + 255) / 256 * 256) * I;
+  // MX: one 1 KB exponent tile per 32 KB code tile
+  L.size[MOE_REGION_W13S] = mx ? L.size[MOE_REGION_W13T] / 32 : 0;
+  L.size[MOE_REGION_W2S] = mx ? L.size[MOE_REGION_W2T] / 32 : 0;
   L.size[kRegionBlkBase] = L.compact_blocks * E * 4;
   size_t off = 0;
   for (int r = 0; r < kNumRegions; ++r) {

@@ -11,8 +11,8 @@ namespace moe {
 
 constexpr int kMaxExperts = 1024;
 constexpr int kCompactChunk = 4096;  // routes per compaction workgroup (256 lanes x 16)
-constexpr int kNumRegions = 16;
-constexpr int kRegionBlkBase = 15;   // internal: per-(compaction block, expert) bases
+constexpr int kNumRegions = 18;
+constexpr int kRegionBlkBase = 17;   // internal: per-(compaction block, expert) bases
 
 // Words of the device header (MOE_REGION_STATUS).
 enum HeaderWord : int {
@@ -64,8 +64,10 @@ struct StageArgs {
   uint32_t* hdr;
   int32_t* staged_idx;
   float* staged_w;
-  uint8_t* xq;            // e4m3 rows (or bf16 rows for the MX variant)
-  float* xs;
+  uint8_t* xq;            // e4m3 rows; MX variant: hi-term plane then lo-term plane
+  float* xs;              // 1x128 float32 scales (FP8 path)
+  int64_t x_plane;        // MX variant: bytes from the hi-term plane to the lo-term plane
+  uint32_t* xs_mx;        // MX variant: packed E8M0 exponents [rows, H/32] (byte 0 hi, byte 1 lo)
 };
 int launch_stage(const StageArgs& a, void* stream);
 
@@ -113,6 +115,31 @@ int launch_fc1(const GemmArgs& a, int block_m, void* stream);
 int launch_fc2(const GemmArgs& a, int block_m, void* stream);
 int gemm_max_workgroups_per_cu(int which, int block_m);
 
+// MXFP8-weight x BF16-activation GEMMs (moe_gemm_mx.hip).  Activations are
+// held as two e4m3 terms with their own E8M0 exponent per 32 K-elements.
+struct MxGemmArgs {
+  const uint8_t* a;          // hi-term rows; the lo-term rows are a_plane bytes further
+  int64_t a_plane;
+  const uint32_t* a_scale;   // [rows, K/32] packed E8M0 (byte 0 hi term, byte 1 lo term)
+  int32_t a_mode;            // 0: sorted position p; 1: token = route/K
+  const int32_t* sorted_route;
+  int32_t top_k;
+  const uint8_t* w;          // e4m3 weight tiles, MX operand order ([E, n_tiles, K/128] x 32 KB)
+  const uint32_t* w_scale;   // E8M0 weight scale tiles ([E, n_tiles, K/128] x 256 words)
+  int32_t n_rows, k_dim, inter, n_tiles;
+  const int32_t* tiles;
+  const int32_t* offsets;
+  const uint32_t* hdr;
+  uint8_t* hq;               // FC1: hi-term rows [R, I]; lo-term rows h_plane bytes further
+  int64_t h_plane;
+  uint32_t* hs;              // FC1: packed E8M0 [R, I/32]
+  uint16_t* y;               // FC2: bf16 [R, H]
+  int32_t grid;
+};
+int launch_fc1_mx(const MxGemmArgs& a, int block_m, void* stream);
+int launch_fc2_mx(const MxGemmArgs& a, int block_m, void* stream);
+int gemm_mx_max_workgroups_per_cu(int which, int block_m);
+
 struct CombineArgs {
   const uint16_t* y;
   const int32_t* route_pos;
@@ -123,6 +150,8 @@ struct CombineArgs {
 int launch_combine(const CombineArgs& a, void* stream);
 
 int launch_tile_weights(const uint8_t* src, uint8_t* dst, int experts, int n_rows, int k_dim, int n_tiles,
-                        int inter, bool fc1, void* stream);
+                        int inter, bool fc1, bool mx_order, void* stream);
+int launch_tile_mx_scales(const uint8_t* src, uint32_t* dst, int experts, int n_rows, int k_dim, int n_tiles,
+                          int inter, bool fc1, void* stream);
 
 }  // namespace moe

@@ -62,6 +62,45 @@ __global__ __launch_bounds__(256) void stage_quant_kernel(StageArgs a, int64_t g
   }
 }
 
+// MXFP8 variant: BF16 rows are kept (not quantised) as the sum of two e4m3
+// terms, each with its own E8M0 exponent per 32 columns, so the scaled MFMA
+// can consume them: hi = e4m3(x / 2^e_hi), lo = e4m3((x - hi * 2^e_hi) / 2^e_lo).
+// Four lanes per 32-column block, eight columns each.  Writes the hi codes
+// to plane 0, the lo codes to plane 1 (x_plane bytes further) and one word
+// (e_hi + 127) | (e_lo + 127) << 8 per block.  Block 0 resets the header.
+__global__ __launch_bounds__(256) void stage_split_kernel(StageArgs a, int64_t groups) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (blockIdx.x == 0 && threadIdx.x < 64) a.hdr[threadIdx.x] = threadIdx.x == kHdrTokens ? (uint32_t)a.tokens : 0u;
+  const int64_t grp = g >> 2;
+  if (grp >= groups) return;
+  const int q = a.hidden >> 5;
+  const int64_t row = grp / q;
+  const int blk = (int)(grp - row * q);
+  const int64_t col = (int64_t)blk * 32 + (threadIdx.x & 3) * 8;
+  const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + row * a.hidden + col);
+  float v[8];
+  v[0] = bf16_to_f32(raw.x & 0xffffu); v[1] = bf16_to_f32(raw.x >> 16);
+  v[2] = bf16_to_f32(raw.y & 0xffffu); v[3] = bf16_to_f32(raw.y >> 16);
+  v[4] = bf16_to_f32(raw.z & 0xffffu); v[5] = bf16_to_f32(raw.z >> 16);
+  v[6] = bf16_to_f32(raw.w & 0xffffu); v[7] = bf16_to_f32(raw.w >> 16);
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  const int e_hi = mx_block_exp(group_max<4>(m));
+  float r[8];
+  const uint32_t h0 = mx_term4(v, e_hi, r), h1 = mx_term4(v + 4, e_hi, r + 4);
+  float mr = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mr = fmaxf(mr, fabsf(r[i]));
+  const int e_lo = mx_block_exp(group_max<4>(mr));
+  float unused[8];
+  const uint32_t l0 = mx_term4(r, e_lo, unused), l1 = mx_term4(r + 4, e_lo, unused + 4);
+  uint8_t* dst = a.xq + row * a.hidden + col;
+  *reinterpret_cast<uint2*>(dst) = make_uint2(h0, h1);
+  *reinterpret_cast<uint2*>(dst + a.x_plane) = make_uint2(l0, l1);
+  if ((threadIdx.x & 3) == 0) a.xs_mx[row * q + blk] = (uint32_t)(e_hi + 127) | ((uint32_t)(e_lo + 127) << 8);
+}
+
 // One thread per token slot row in [0, max_rows).  Live rows are checked and
 // masked; rows past the live count are staged as masked.
 __global__ __launch_bounds__(256) void stage_routes_kernel(StageArgs a) {
@@ -131,11 +170,17 @@ __global__ __launch_bounds__(256) void stage_routes_kernel(StageArgs a) {
 
 int launch_stage(const StageArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t groups = (int64_t)a.tokens * (a.hidden / 128);
-  const int64_t threads = groups * 16;
-  const int qblocks = (int)((threads + 255) / 256);
-  const int copies = (a.flags & MOE_FLAG_PER_ROUTE_STAGING) ? a.top_k : 1;
-  hipLaunchKernelGGL(stage_quant_kernel, dim3(qblocks > 0 ? qblocks : 1), dim3(256), 0, s, a, groups, copies);
+  if (a.act_format == MOE_ACT_BF16) {
+    const int64_t groups = (int64_t)a.tokens * (a.hidden / 32);
+    const int qblocks = (int)((groups * 4 + 255) / 256);
+    hipLaunchKernelGGL(stage_split_kernel, dim3(qblocks > 0 ? qblocks : 1), dim3(256), 0, s, a, groups);
+  } else {
+    const int64_t groups = (int64_t)a.tokens * (a.hidden / 128);
+    const int64_t threads = groups * 16;
+    const int qblocks = (int)((threads + 255) / 256);
+    const int copies = (a.flags & MOE_FLAG_PER_ROUTE_STAGING) ? a.top_k : 1;
+    hipLaunchKernelGGL(stage_quant_kernel, dim3(qblocks > 0 ? qblocks : 1), dim3(256), 0, s, a, groups, copies);
+  }
   hipLaunchKernelGGL(stage_routes_kernel, dim3((a.max_rows + 255) / 256), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

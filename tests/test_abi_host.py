@@ -134,3 +134,18 @@ def test_status_strings():
     for s in range(0, -7, -1):
         assert L.status_string(s).startswith("MOE_")
     assert L.status_string(-99) == "MOE_ERR_UNKNOWN"
+
+
+def test_query_mx_variant_sizes():
+    """MXFP8 x BF16: two e4m3 activation terms, one E8M0 word per 32 columns,
+    and 1 KB of tiled weight exponents per 32 KB weight tile."""
+    T, H, I, E, K = 4096, 7168, 2048, 32, 8
+    fp8 = L.moe_workspace_query(_cfg(), 128, T, 1.0)
+    mx = L.moe_workspace_query(_cfg(weight_format=L.MOE_WEIGHT_MXFP8_E4M3, act_format=L.MOE_ACT_BF16), 128, T, 1.0)
+    R = T * K
+    extra = (T * H                                   # lo-term plane of x
+             + T * (H // 32) * 4 - T * (H // 128) * 4  # exponent words vs 1x128 scales
+             + R * I                                 # lo-term plane of h
+             + R * (I // 32) * 4 - R * (I // 128) * 4
+             + E * 2 * I * H // 32 + E * H * I // 32)  # weight exponent tiles
+    assert abs((mx - fp8) - extra) <= 8 * 256  # region alignment only
