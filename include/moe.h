@@ -126,7 +126,8 @@ typedef struct {
   int32_t grid_fc2;
   int32_t row_cap;       /* route rows the workspace holds */
   int32_t max_m_tiles;   /* bound on (expert, row-tile) pairs */
-  int32_t reserved;
+  int32_t tile_order;    /* weight tile order in MOE_REGION_W13T/W2T: 0 16x16x128 fragments,
+                            1 MX-scaled operand order */
 } moe_tactic_t;
 
 /* Workspace regions exposed for inspection (moe_layer_region). */

@@ -71,7 +71,7 @@ class moe_weights_t(Structure):
 class moe_tactic_t(Structure):
     _fields_ = [
         ("token_bucket", c_int32), ("block_m", c_int32), ("block_n", c_int32), ("grid_fc1", c_int32),
-        ("grid_fc2", c_int32), ("row_cap", c_int32), ("max_m_tiles", c_int32), ("reserved", c_int32),
+        ("grid_fc2", c_int32), ("row_cap", c_int32), ("max_m_tiles", c_int32), ("tile_order", c_int32),
     ]
 
 
@@ -174,7 +174,7 @@ def moe_layer_region(layer: int, region: int):
 def moe_layer_tactic(layer: int) -> dict:
     t = moe_tactic_t()
     _check(_lib.moe_layer_tactic(layer, ctypes.byref(t)))
-    return {name: getattr(t, name) for name, _ in t._fields_ if name != "reserved"}
+    return {name: getattr(t, name) for name, _ in t._fields_}
 
 
 def moe_profile_enable(layer: int, enable: bool) -> None:

@@ -143,10 +143,11 @@ extern "C" moe_status_t moe_layer_create(const moe_config_t* cfg, int32_t expect
   uint8_t* w13t = l->ws + L.off[MOE_REGION_W13T];
   uint8_t* w2t = l->ws + L.off[MOE_REGION_W2T];
   const int E = cfg->num_experts, H = cfg->hidden, I = cfg->intermediate;
-  bool ok = moe::launch_tile_weights(static_cast<const uint8_t*>(w->w13), w13t, E, 2 * I, H, I / 128, I, true, mx,
+  const int order = mx ? moe::kTileOrderMx : moe::kTileOrder16;
+  bool ok = moe::launch_tile_weights(static_cast<const uint8_t*>(w->w13), w13t, E, 2 * I, H, I / 128, I, true, order,
                                      stream) == 0 &&
-            moe::launch_tile_weights(static_cast<const uint8_t*>(w->w2), w2t, E, H, I, (H + 255) / 256, I, false, mx,
-                                     stream) == 0;
+            moe::launch_tile_weights(static_cast<const uint8_t*>(w->w2), w2t, E, H, I, (H + 255) / 256, I, false,
+                                     order, stream) == 0;
   if (ok && mx)
     ok = moe::launch_tile_mx_scales(static_cast<const uint8_t*>(w->w13_scale),
                                     reinterpret_cast<uint32_t*>(l->ws + L.off[MOE_REGION_W13S]), E, 2 * I, H, I / 128,
@@ -368,7 +369,7 @@ extern "C" moe_status_t moe_layer_tactic(const moe_layer_t* l, moe_tactic_t* t) 
   t->grid_fc2 = l->grid_fc2;
   t->row_cap = (int32_t)l->L.row_cap;
   t->max_m_tiles = (int32_t)l->L.max_m_tiles;
-  t->reserved = 0;
+  t->tile_order = l->cfg.weight_format == MOE_WEIGHT_MXFP8_E4M3 ? moe::kTileOrderMx : moe::kTileOrder16;
   return MOE_OK;
 }
 

@@ -47,6 +47,7 @@ namespace moe {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -92,6 +93,25 @@ __device__ __forceinline__ v8i lds_frag(const lds_u8* p) {
   return r;
 }
 
+// Token operand layout in LDS, per 16-token block (2 KB): the 128-byte
+// K-block of token t is 8 chunks of 16 bytes, and chunk c of token t sits at
+// position 8 t + (c ^ tok_swz(t)).  One DMA instruction then fills 64
+// consecutive positions = 8 whole token rows, one 128-byte line each (gathers
+// of partial lines run at a fraction of the L2 rate), and the fragment reads
+// (lane l: token l % 16, chunk 2 (l / 16) + half) hit 16 distinct 16-byte
+// bank groups in every 8 and every 16 consecutive lanes.
+__device__ __forceinline__ int tok_swz(int t) { return (t & 7) ^ ((t >> 3) & 1); }
+
+// Fragment whose "lo" and "hi" 16 bytes come from two per-lane addresses.
+__device__ __forceinline__ v8i lds_frag2(const lds_u8* lo_p, const lds_u8* hi_p) {
+  const u32x4 lo = *reinterpret_cast<lds_u32x4*>(lo_p);
+  const u32x4 hi = *reinterpret_cast<lds_u32x4*>(hi_p);
+  v8i r;
+  r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];
+  r[4] = (int)hi[0]; r[5] = (int)hi[1]; r[6] = (int)hi[2]; r[7] = (int)hi[3];
+  return r;
+}
+
 // LDS-DMA (global_load_lds): lane L's bytes land at lds_wave_base + L * size;
 // lds_wave_base is wave-uniform and goes through M0.  Issued as inline asm so
 // the compiler's wait insertion, which cannot follow which ring stage a DMA
@@ -117,6 +137,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Workgroup barrier without a memory fence (no implied wait on the ring).
 __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
+
+// Wait for this wave's LDS accesses (the ratio writes before a barrier).
+__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <int BT>
 struct Cfg {
@@ -149,7 +172,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring1[C::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t ring2[C::STAGES > 2 ? C::STAGE : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t ring3[C::STAGES > 3 ? C::STAGE : 16];
-  __shared__ __attribute__((aligned(16))) float wsc[2 * kMaxKBlocks];  // [block 0 | block 1][kb]
+  __shared__ __attribute__((aligned(16))) float wsc[2 * kMaxKBlocks];  // weight scales [block 0 | block 1][kb]
+  __shared__ __attribute__((aligned(16))) float sx0[BT];               // token scales of K-block 0
+  __shared__ __attribute__((aligned(16))) float rsc[2][BT][2];          // promotion ratios, double-buffered
+  __shared__ __attribute__((aligned(16))) float fsc[BT][2];             // final scale products
   auto ring = [&](auto stage) -> lds_u8* {
     constexpr int S = decltype(stage)::value;
     if constexpr (S == 0) return (lds_u8*)ring0;
@@ -172,10 +198,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
   const int slot = blockIdx.x >> 3;
   const int per_xcd = gridDim.x >> 3;
   const int64_t v_begin = total * xcd / 8, v_end = total * (xcd + 1) / 8;
-  // lane's offset of its first weight block, token block and token scale
+  // lane's offset of its first weight block and (two halves of) token block
   const uint32_t a_lane = (uint32_t)(wn * (C::G / 16)) * 2048u + (uint32_t)lane * 16u;
-  const uint32_t b_lane = (uint32_t)(wt * C::TBW) * 2048u + (uint32_t)lane * 16u;
-  const uint32_t s_lane = (uint32_t)(wt * C::TBW * 16 + (lane & 15));
+  const int tl = lane & 15;
+  const uint32_t b_lane0 = (uint32_t)(wt * C::TBW) * 2048u + 16u * (uint32_t)(8 * tl + ((2 * (lane >> 4)) ^ tok_swz(tl)));
+  const uint32_t b_lane1 =
+      (uint32_t)(wt * C::TBW) * 2048u + 16u * (uint32_t)(8 * tl + ((2 * (lane >> 4) + 1) ^ tok_swz(tl)));
+  const int t_lane = wt * C::TW + tl;  // token of this lane's outputs in token block 0
+  // Promotion role: thread (pb, pt) keeps the running scale product
+  // F = sx[pt] * sw[pb] of weight block pb (gate / first 128 rows or up /
+  // second) for token pt, and publishes r = F_prev / F_next per K-block.
+  const bool prole = tid < 2 * BT;
+  const int pt = tid % BT, pb = (tid / BT) & 1;
 
   for (int64_t v = v_begin + slot; v < v_end; v += per_xcd) {
     // ---- tile coordinates ------------------------------------------------
@@ -209,18 +243,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
       const int r = a.sorted_route[p];
       return a.a_mode == 2 ? r : r / a.top_k;
     };
-    // tokens: virtual lane V of the tile covers fragment piece V/64
+    // tokens: LDS position V (16 bytes) of the stage holds chunk
+    // (V % 8) ^ tok_swz(token) of token V / 8 (see tok_swz)
     const uint8_t* b_src[C::B_INSTR];
 #pragma unroll
     for (int j = 0; j < C::B_INSTR; ++j) {
       const int v = wave * BT + j * 64 + (lane < C::B_LANES ? lane : 0);
-      const int piece = v >> 6, lp = v & 63;
-      const int t = (piece >> 1) * 16 + (lp & 15);
-      const int chunk = 2 * (lp >> 4) + (piece & 1);
+      const int t = v >> 3;
+      const int chunk = (v & 7) ^ tok_swz(t & 15);
       b_src[j] = a.a + src_row(t) * a.k_dim + chunk * 16;
     }
+    // token scales: a stage carries those of the next K-block (the promotion
+    // threads turn them into ratios one K-block ahead of their use)
     const float* s_src = a.a_scale + src_row(wave * C::S_LANES + (lane < C::S_LANES ? lane : 0)) * kbs;
-    // this tile's two weight-scale columns, DMA'd once per tile (waves 0-3)
+    // once per tile: this tile's two weight-scale columns (waves 0-3) and the
+    // token scales of K-block 0; both are older than every stage load, so the
+    // first stage's wait covers them
     if (wave < 4) {
       const int blk = wave >> 1, half = wave & 1;
       const int kb = half * 64 + lane;
@@ -228,6 +266,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
         dma4(a.w_scale + ((int64_t)e * nblk_w + (blk ? nb1 : nb0)) * kbs + kb,
              (const lds_u8*)wsc + (blk * kMaxKBlocks + half * 64) * 4);
     }
+    if (lane < C::S_LANES) dma4(s_src, (const lds_u8*)sx0 + wave * C::S_LANES * 4);
+    // K-block 0 meets a zero accumulator: any finite ratio will do
+    if (prole) rsc[0][pt][pb] = 0.0f;
+    float pf = 1.0f;
 
     auto issue = [&](auto stage, int kb) {
       const lds_u8* As = ring(stage);
@@ -239,30 +281,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < C::B_INSTR; ++j)
         if (lane < C::B_LANES) dma16(b_src[j] + kb * kKB, Bs + (wave * BT + j * 64) * 16);
-      if (lane < C::S_LANES) dma4(s_src + kb, Ss + wave * C::S_LANES * 4);
+      if (lane < C::S_LANES) dma4(s_src + min(kb + 1, kbs - 1), Ss + wave * C::S_LANES * 4);
     };
 
     v4f acc[C::NB][C::TBW];
-    float fs0[C::TBW], fs1[C::TBW];  // current scale product per token block (gate/first, up/second)
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
       for (int tb = 0; tb < C::TBW; ++tb) acc[nb][tb] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int tb = 0; tb < C::TBW; ++tb) fs0[tb] = fs1[tb] = 1.0f;
 
     // ---- K loop: STAGES-deep LDS ring -------------------------------------
+    // acc holds sum_{j <= kb} P_j * F_j / F_kb for block products P_j; before
+    // block kb's MFMAs it is rescaled by r_kb = F_{kb-1} / F_kb, and after the
+    // loop multiplied by F_last.
     auto step = [&](auto stage, int kb) {
       constexpr int ST = decltype(stage)::value;
       const int ahead = min(C::STAGES - 2, kbs - 1 - kb);  // stages issued after this one
       if (C::STAGES >= 4 && ahead >= 2) wait_vmcnt<(C::STAGES >= 4 ? 2 : 0) * C::N_LD>();
       else if (C::STAGES >= 3 && ahead >= 1) wait_vmcnt<(C::STAGES >= 3 ? 1 : 0) * C::N_LD>();
       else wait_vmcnt<0>();
-      // Every wave has its own DMA for this stage complete; the barrier makes
-      // that true for all waves.  It also orders the previous stage's LDS
-      // reads (consumed by MFMAs already) before the DMA issued next into it.
-      // A plain s_barrier: a fenced barrier would also drain the DMA of the
-      // stages still in flight.
+      // Every wave has its own DMA for this stage complete and its ratio
+      // writes of the previous step done; the barrier makes that true for
+      // all waves.  It also orders the previous stage's LDS reads (consumed
+      // by MFMAs already) before the DMA issued next into it.  A plain
+      // s_barrier: a fenced barrier would also drain the DMA of the stages
+      // still in flight.
+      wait_lgkmcnt0();
       barrier_nofence();
       if (kb + C::STAGES - 1 < kbs)
         issue(std::integral_constant<int, (ST + C::STAGES - 1) % C::STAGES>{}, kb + C::STAGES - 1);
@@ -270,12 +314,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
       const lds_u8* As = ring(stage);
       const lds_u8* Bs = As + C::A_BYTES;
       const lds_f32* Ss = (const lds_f32*)(Bs + C::B_BYTES);
-      const float sw0 = wscl[kb], sw1 = wscl[kMaxKBlocks + kb];
-      // Per-lane operand bases (wave/lane part computed once per kernel):
-      // every fragment read below is base + compile-time offset.
       const lds_u8* Ap = As + a_lane;
-      const lds_u8* Bp = Bs + b_lane;
-      const lds_f32* Sp = Ss + s_lane;
+      const lds_u8* Bp0 = Bs + b_lane0;
+      const lds_u8* Bp1 = Bs + b_lane1;
+      typedef __attribute__((address_space(3))) const v2f lds_v2f;
+      const lds_v2f* Rp = (const lds_v2f*)((const lds_f32*)&rsc[kb & 1][0][0] + 2 * t_lane);
       auto aoff = [](int nb) {  // byte offset of weight block nb of this wave
         return (nb < C::NB / 2 ? nb : 8 - C::NB / 2 + nb) * 2048;
       };
@@ -284,26 +327,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
         // The scheduling barrier keeps the compiler from hoisting every
         // block's LDS reads to the top (all of them live at once).
         v8i bq[C::TBW];
-        float r0[C::TBW], r1[C::TBW];
+        v2f rr[C::TBW];
 #pragma unroll
         for (int tb = 0; tb < C::TBW; ++tb) {
-          bq[tb] = lds_frag(Bp + tb * 2048);
-          const float sx = Sp[tb * 16];
-          const float g0 = carry_scale(sx * sw0, fs0[tb]), g1 = carry_scale(sx * sw1, fs1[tb]);
-          r0[tb] = fs0[tb] * __builtin_amdgcn_rcpf(g0);
-          r1[tb] = fs1[tb] * __builtin_amdgcn_rcpf(g1);
-          fs0[tb] = g0;
-          fs1[tb] = g1;
+          bq[tb] = lds_frag2(Bp0 + tb * 2048, Bp1 + tb * 2048);
+          rr[tb] = Rp[tb * 16];
         }
         v8i aq = lds_frag(Ap + aoff(0));
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) {
           const v8i an = lds_frag(Ap + aoff(nb + 1 < C::NB ? nb + 1 : nb));
 #pragma unroll
-          for (int tb = 0; tb < C::TBW; ++tb) {
-            const float r = nb < C::NB / 2 ? r0[tb] : r1[tb];
-            acc[nb][tb] = mfma_fp8(aq, bq[tb], acc[nb][tb] * r);
-          }
+          for (int tb = 0; tb < C::TBW; ++tb)
+            acc[nb][tb] = mfma_fp8(aq, bq[tb], acc[nb][tb] * (nb < C::NB / 2 ? rr[tb].x : rr[tb].y));
           __builtin_amdgcn_sched_barrier(0);
           aq = an;
         }
@@ -312,22 +348,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
         v8i aq[C::NB];
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) aq[nb] = lds_frag(Ap + aoff(nb));
-        v8i bq = lds_frag(Bp);
-        float sx = Sp[0];
+        v8i bq = lds_frag2(Bp0, Bp1);
+        v2f rr = Rp[0];
 #pragma unroll
         for (int tb = 0; tb < C::TBW; ++tb) {
           const int tn = tb + 1 < C::TBW ? tb + 1 : tb;
-          const v8i bn = lds_frag(Bp + tn * 2048);
-          const float sn = Sp[tn * 16];
-          const float g0 = carry_scale(sx * sw0, fs0[tb]), g1 = carry_scale(sx * sw1, fs1[tb]);
-          const float r0 = fs0[tb] * __builtin_amdgcn_rcpf(g0), r1 = fs1[tb] * __builtin_amdgcn_rcpf(g1);
-          fs0[tb] = g0;
-          fs1[tb] = g1;
+          const v8i bn = lds_frag2(Bp0 + tn * 2048, Bp1 + tn * 2048);
+          const v2f rn = Rp[tn * 16];
 #pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb) acc[nb][tb] = mfma_fp8(aq[nb], bq, acc[nb][tb] * (nb < C::NB / 2 ? r0 : r1));
+          for (int nb = 0; nb < C::NB; ++nb) acc[nb][tb] = mfma_fp8(aq[nb], bq, acc[nb][tb] * (nb < C::NB / 2 ? rr.x : rr.y));
           __builtin_amdgcn_sched_barrier(0);
           bq = bn;
-          sx = sn;
+          rr = rn;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // promotion threads: ratios of K-block kb + 1 (read by every wave at
+      // the next step)
+      if (prole) {
+        const float swb_kb = wscl[pb * kMaxKBlocks + kb];
+        if (kb == 0) pf = carry_scale(((const lds_f32*)sx0)[pt] * swb_kb, 1.0f);
+        if (kb + 1 < kbs) {
+          const float fn = carry_scale(Ss[pt] * wscl[pb * kMaxKBlocks + kb + 1], pf);
+          rsc[(kb + 1) & 1][pt][pb] = pf * __builtin_amdgcn_rcpf(fn);
+          pf = fn;
         }
       }
     };
@@ -340,15 +384,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
       if (C::STAGES > 2 && kb + 2 < kbs) step(std::integral_constant<int, (C::STAGES > 2 ? 2 : 0)>{}, kb + 2);
       if (C::STAGES > 3 && kb + 3 < kbs) step(std::integral_constant<int, (C::STAGES > 3 ? 3 : 0)>{}, kb + 3);
     }
+    if (prole) fsc[pt][pb] = pf;
+    __syncthreads();  // every wave is done with the ring (and fsc is visible) before the epilogue
     // undo the running scale: acc = sum_kb F_kb * (block product)
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
+    for (int tb = 0; tb < C::TBW; ++tb) {
+      const v2f f = ((const __attribute__((address_space(3))) v2f*)((const lds_f32*)&fsc[0][0]))[t_lane + tb * 16];
 #pragma unroll
-      for (int tb = 0; tb < C::TBW; ++tb) acc[nb][tb] *= (nb < C::NB / 2 ? fs0[tb] : fs1[tb]);
-    __syncthreads();  // every wave is done with the ring before the epilogue reuses LDS
+      for (int nb = 0; nb < C::NB; ++nb) acc[nb][tb] *= (nb < C::NB / 2 ? f.x : f.y);
+    }
 
     // ---- epilogue -----------------------------------------------------------
     if (FC1) {
+      // h = silu(gate) * up = g / (1 + 2^(-g log2 e)) * up on the hardware
+      // exp2 and reciprocal; then the 1x128 amax, s = amax / 448 and the
+      // codes of h * (1 / s).
       float* red = reinterpret_cast<float*>(smem);  // [WN][BT] partial amax
       float hv[C::TBW][C::NB / 2][4];
 #pragma unroll
@@ -359,7 +409,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float gt = acc[g][tb][i], up = acc[C::NB / 2 + g][tb][i];
-            const float h = gt / (1.0f + expf(-gt)) * up;
+            const float h = gt * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gt * 1.44269504f)) * up;
             hv[tb][g][i] = h;
             m = fmaxf(m, fabsf(h));
           }
@@ -376,17 +426,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
 #pragma unroll
         for (int w = 0; w < C::WN; ++w) amax = fmaxf(amax, red[w * BT + t]);
         const float s = amax / kE4m3Max;
+        const float inv = s != 0.f ? kE4m3Max * __builtin_amdgcn_rcpf(amax) : 0.f;
         if (t < rows_valid) {
           uint8_t* dst = a.hq + (int64_t)(p0 + t) * a.inter + nt * 128 + wn * C::G + 4 * (lane >> 4);
 #pragma unroll
           for (int g = 0; g < C::NB / 2; ++g) {
-            uint32_t word = 0;
-            if (s != 0.f) {
-              int w = cvt2_e4m3(hv[tb][g][0] / s, hv[tb][g][1] / s, 0, false);
-              w = cvt2_e4m3(hv[tb][g][2] / s, hv[tb][g][3] / s, w, true);
-              word = (uint32_t)w;
-            }
-            *reinterpret_cast<uint32_t*>(dst + g * 16) = word;
+            int w = cvt2_e4m3(hv[tb][g][0] * inv, hv[tb][g][1] * inv, 0, false);
+            w = cvt2_e4m3(hv[tb][g][2] * inv, hv[tb][g][3] * inv, w, true);
+            *reinterpret_cast<uint32_t*>(dst + g * 16) = (uint32_t)w;
           }
           if (wn == 0 && (lane >> 4) == 0) a.hs[(int64_t)(p0 + t) * ikb + nt] = s;
         }
@@ -415,8 +462,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
 
 template <int BT, bool FC1>
 static int launch_one(const GemmArgs& a, void* stream) {
-  hipLaunchKernelGGL((gemm_fp8_kernel<BT, FC1>), dim3(a.grid), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), a);
+  hipLaunchKernelGGL((gemm_fp8_kernel<BT, FC1>), dim3(a.grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                     a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

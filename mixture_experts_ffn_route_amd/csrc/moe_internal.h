@@ -149,8 +149,11 @@ struct CombineArgs {
 };
 int launch_combine(const CombineArgs& a, void* stream);
 
+// Weight tile orders (moe_weights.hip): 16x16x128 fragments (FP8 path) and
+// the MX-scaled operand order (MXFP8 path).
+enum TileOrder : int { kTileOrder16 = 0, kTileOrderMx = 1 };
 int launch_tile_weights(const uint8_t* src, uint8_t* dst, int experts, int n_rows, int k_dim, int n_tiles,
-                        int inter, bool fc1, bool mx_order, void* stream);
+                        int inter, bool fc1, int order, void* stream);
 int launch_tile_mx_scales(const uint8_t* src, uint32_t* dst, int experts, int n_rows, int k_dim, int n_tiles,
                           int inter, bool fc1, void* stream);
 

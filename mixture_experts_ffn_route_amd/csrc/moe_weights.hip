@@ -24,6 +24,7 @@
 // equal byte positions of both operands, so either order gives its product.
 // Scale tile (e, nt, kb) = 4 groups x 64 lanes x 4 bytes: group q, lane l,
 // byte b holds the exponent of row block 4q+b, row l%16, 32-block l/16.
+
 #include <hip/hip_runtime.h>
 
 #include "moe_internal.h"
@@ -35,27 +36,25 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // One thread per 16-byte chunk of the destination.
 __global__ __launch_bounds__(256) void tile_weights_kernel(const uint8_t* src, uint8_t* dst, int64_t chunks,
                                                            int n_rows, int k_dim, int n_tiles, int inter,
-                                                           int fc1, int mx_order) {
+                                                           int fc1, int order) {
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (c >= chunks) return;
   const int kbs = k_dim / 128;
   const int lane = (int)(c & 63);
   const int hilo = (int)((c >> 6) & 1);
-  const int rb = (int)((c >> 7) & 15);
   const int64_t tile = c >> 11;  // 2048 chunks per (e, nt, kb) tile
   const int kb = (int)(tile % kbs);
   const int nt = (int)((tile / kbs) % n_tiles);
   const int64_t e = tile / ((int64_t)kbs * n_tiles);
+  const int rb = (int)((c >> 7) & 15);
   int row;
   if (fc1)
     row = (rb < 8 ? nt * 128 + rb * 16 : inter + nt * 128 + (rb - 8) * 16) + (lane & 15);
   else
     row = nt * 256 + rb * 16 + (lane & 15);
+  const int kbyte = kb * 128 + (order == kTileOrderMx ? 16 * (lane >> 4) + 64 * hilo : 32 * (lane >> 4) + 16 * hilo);
   u32x4 v = {0u, 0u, 0u, 0u};
-  if (row < n_rows) {
-    const int kbyte = kb * 128 + (mx_order ? 16 * (lane >> 4) + 64 * hilo : 32 * (lane >> 4) + 16 * hilo);
-    v = *reinterpret_cast<const u32x4*>(src + (e * n_rows + row) * (int64_t)k_dim + kbyte);
-  }
+  if (row < n_rows) v = *reinterpret_cast<const u32x4*>(src + (e * n_rows + row) * (int64_t)k_dim + kbyte);
   *reinterpret_cast<u32x4*>(dst + c * 16) = v;
 }
 
@@ -88,11 +87,11 @@ __global__ __launch_bounds__(256) void tile_mx_scales_kernel(const uint8_t* src,
 }
 
 int launch_tile_weights(const uint8_t* src, uint8_t* dst, int experts, int n_rows, int k_dim, int n_tiles,
-                        int inter, bool fc1, bool mx_order, void* stream) {
+                        int inter, bool fc1, int order, void* stream) {
   const int64_t chunks = (int64_t)experts * n_tiles * (k_dim / 128) * 2048;
   const int64_t blocks = (chunks + 255) / 256;
   hipLaunchKernelGGL(tile_weights_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream), src,
-                     dst, chunks, n_rows, k_dim, n_tiles, inter, fc1 ? 1 : 0, mx_order ? 1 : 0);
+                     dst, chunks, n_rows, k_dim, n_tiles, inter, fc1 ? 1 : 0, order);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

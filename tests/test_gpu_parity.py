@@ -109,14 +109,15 @@ def test_ragged_token_counts(tokens):
         assert_output_close(_bits(out), res.out_bits, f"T={tokens}")
 
 
-@pytest.mark.parametrize("expected_m", [8, 48, 4096])
-def test_tactics_agree_bit_exact(expected_m):
-    """Every tile tactic computes the same bits (per-row arithmetic is tile-independent)."""
+@pytest.mark.parametrize("pair", [(8, 48), (2, 24), (96, 4096), (128, 200), (8, 4096)])
+def test_tactics_agree_bit_exact(pair):
+    """Every token tile (16 to 256 tokens) computes the same bits: each
+    output's arithmetic is tile-independent."""
     shape = CONFIGS["small"]
     inp = make_layer_inputs(shape, seed=1)
     dev = to_device(inp)
     outs = []
-    for em in (expected_m, 96):
+    for em in pair:
         layer = make_layer(shape, dev, expected_m=em)
         outs.append(_bits(run_forward(layer, dev)))
     assert np.array_equal(outs[0], outs[1])
@@ -227,7 +228,7 @@ def test_skewed_zipf_sampled():
 
 
 def _retile(w, fc1, inter):
-    """NumPy statement of the kernels' weight tile order (see moe_weights.hip)."""
+    """NumPy statement of the 16x16x128 weight tile order (see moe_weights.hip)."""
     E, N, K = w.shape
     n_tiles = inter // 128 if fc1 else (N + 255) // 256
     kbs = K // 128
@@ -249,14 +250,17 @@ def _retile(w, fc1, inter):
     return out.reshape(-1)
 
 
-@pytest.mark.parametrize("shape", [CONFIGS["tiny"], MoEShape(16, 384, 256, 4, 2, "topk")])
-def test_create_time_weight_tiling_is_exact(shape):
+@pytest.mark.parametrize("shape,expected_m", [(CONFIGS["tiny"], None), (MoEShape(16, 384, 256, 4, 2, "topk"), None),
+                                              (MoEShape(16, 384, 256, 4, 2, "topk"), 200),
+                                              (MoEShape(16, 256, 128, 8, 2, "topk"), 1000)])
+def test_create_time_weight_tiling_is_exact(shape, expected_m):
     inp = make_layer_inputs(shape, seed=8)
     dev = to_device(inp)
-    layer = make_layer(shape, dev)
+    layer = make_layer(shape, dev, expected_m=expected_m)
     torch.cuda.synchronize()
     w13t = _np(layer.region("w13t", torch.uint8))
     w2t = _np(layer.region("w2t", torch.uint8))
+    assert layer.tactic()["tile_order"] == 0
     assert np.array_equal(w13t, _retile(inp.w13, True, shape.intermediate))
     assert np.array_equal(w2t, _retile(inp.w2, False, shape.intermediate))
     run = run_forward(layer, dev)
