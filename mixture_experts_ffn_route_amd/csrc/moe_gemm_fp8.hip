@@ -56,6 +56,7 @@ constexpr int kWaves = 8;
 constexpr int kBN = 256;          // weight rows per tile
 constexpr int kKB = 128;          // bytes (= e4m3 elements) per K-block
 constexpr int kGroupM = 4;        // token tiles per XCD-local group
+constexpr int kPrefetchAhead = 3; // weight K-blocks prefetched into L2 ahead of the stage loads
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kMaxKBlocks = 128;  // K <= 16384
 constexpr int kWsBytes = 2 * kMaxKBlocks * 4;  // per-tile weight-scale columns
@@ -158,7 +159,7 @@ struct Cfg {
   static constexpr int B_INSTR = (BT + 63) / 64;                  // token-chunk loads per wave
   static constexpr int B_LANES = BT < 64 ? BT : 64;
   static constexpr int S_LANES = BT / kWaves;                     // scale loads per wave
-  static constexpr int N_LD = A_INSTR + B_INSTR + 1;              // vector loads per wave per stage
+  static constexpr int N_LD = A_INSTR + B_INSTR + 2;              // vector loads per wave per stage
   static_assert(TBW >= 1 && NB >= 2 && STAGES >= 2, "tile shape");
   static_assert((STAGES - 2) * N_LD < 64, "vmcnt range");
 };
@@ -176,6 +177,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) float sx0[BT];               // token scales of K-block 0
   __shared__ __attribute__((aligned(16))) float rsc[2][BT][2];          // promotion ratios, double-buffered
   __shared__ __attribute__((aligned(16))) float fsc[BT][2];             // final scale products
+  __shared__ __attribute__((aligned(16))) uint32_t l2sink[kThreads];    // L2 prefetch landing words (never read)
   auto ring = [&](auto stage) -> lds_u8* {
     constexpr int S = decltype(stage)::value;
     if constexpr (S == 0) return (lds_u8*)ring0;
@@ -256,6 +258,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
     // token scales: a stage carries those of the next K-block (the promotion
     // threads turn them into ratios one K-block ahead of their use)
     const float* s_src = a.a_scale + src_row(wave * C::S_LANES + (lane < C::S_LANES ? lane : 0)) * kbs;
+    // L2 prefetch of weights kPrefetchAhead K-blocks ahead of the stage
+    // being loaded: the gm token tiles of a group share this weight tile
+    // (they run side by side on one XCD), so each prefetches every gm-th of
+    // its 256 lines; one word per line lands in l2sink.  Weight K-blocks are
+    // first touches (the token rows are L2 hits by then), and a stage waits
+    // for its slowest load.
+    const int pf_lanes = 32 / gm;  // lines per wave per K-block
+    const int pf_line = (wave * pf_lanes + (lane < pf_lanes ? lane : 0)) * gm + (mt - m0);
+    const uint8_t* pf_src = a.w + ((int64_t)e * a.n_tiles + nt) * kbs * (int64_t)C::A_BYTES + pf_line * 128;
     // once per tile: this tile's two weight-scale columns (waves 0-3) and the
     // token scales of K-block 0; both are older than every stage load, so the
     // first stage's wait covers them
@@ -282,6 +293,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
       for (int j = 0; j < C::B_INSTR; ++j)
         if (lane < C::B_LANES) dma16(b_src[j] + kb * kKB, Bs + (wave * BT + j * 64) * 16);
       if (lane < C::S_LANES) dma4(s_src + min(kb + 1, kbs - 1), Ss + wave * C::S_LANES * 4);
+      if (lane < pf_lanes)
+        dma4(reinterpret_cast<const float*>(pf_src + (int64_t)min(kb + kPrefetchAhead, kbs - 1) * C::A_BYTES),
+             (const lds_u8*)l2sink + wave * 256);
     };
 
     v4f acc[C::NB][C::TBW];
