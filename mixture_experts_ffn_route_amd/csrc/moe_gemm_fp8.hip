@@ -178,6 +178,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) float rsc[2][BT][2];          // promotion ratios, double-buffered
   __shared__ __attribute__((aligned(16))) float fsc[BT][2];             // final scale products
   __shared__ __attribute__((aligned(16))) uint32_t l2sink[kThreads];    // L2 prefetch landing words (never read)
+  __shared__ __attribute__((aligned(16))) float red_s[FC1 ? C::WN * BT : 4];  // FC1 epilogue: partial amax
   auto ring = [&](auto stage) -> lds_u8* {
     constexpr int S = decltype(stage)::value;
     if constexpr (S == 0) return (lds_u8*)ring0;
@@ -185,7 +186,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
     else if constexpr (S == 2) return (lds_u8*)ring2;
     else return (lds_u8*)ring3;
   };
-  uint8_t* smem = ring0;  // epilogue scratch
   const lds_f32* wscl = (const lds_f32*)wsc;
 
   const int tid = threadIdx.x;
@@ -213,20 +213,33 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
   const bool prole = tid < 2 * BT;
   const int pt = tid % BT, pb = (tid / BT) & 1;
 
-  for (int64_t v = v_begin + slot; v < v_end; v += per_xcd) {
-    // ---- tile coordinates ------------------------------------------------
+  // ---- tile state -----------------------------------------------------------
+  // Coordinates and per-lane DMA sources of the tile whose loads are in
+  // flight.  They are set one tile ahead: the next tile's first stages are
+  // issued before the current tile's epilogue, which then hides their latency.
+  int e = 0, p0 = 0, rows_valid = 1, nt = 0, mt = 0, m0 = 0, gm = 1, nb0 = 0, nb1 = 0, pf_lanes = 8;
+  const uint8_t* a_src = a.w;
+  const uint8_t* b_src[C::B_INSTR];
+  const float* s_src = a.a_scale;
+  const uint8_t* pf_src = a.w;
+  auto src_row = [&](int t) -> int64_t {
+    const int p = p0 + min(t, rows_valid - 1);
+    if (!FC1) return p;
+    const int r = a.sorted_route[p];
+    return a.a_mode == 2 ? r : r / a.top_k;
+  };
+  auto setup = [&](int64_t v) {
     const int64_t group = v / ((int64_t)kGroupM * a.n_tiles);
     const int64_t rem = v - group * kGroupM * a.n_tiles;
-    const int m0 = (int)(group * kGroupM);
-    const int gm = min(kGroupM, total_m - m0);
-    const int nt = (int)(rem / gm);
-    const int mt = m0 + (int)(rem % gm);
+    m0 = (int)(group * kGroupM);
+    gm = min(kGroupM, total_m - m0);
+    nt = (int)(rem / gm);
+    mt = m0 + (int)(rem % gm);
     // tile scalars are wave-uniform; saying so keeps their dependents
     // (weight-scale addresses) on the scalar unit
-    const int e = __builtin_amdgcn_readfirstlane(a.tiles[2 * mt]);
-    const int p0 = __builtin_amdgcn_readfirstlane(a.tiles[2 * mt + 1]);
-    const int rows_valid = min(BT, __builtin_amdgcn_readfirstlane(a.offsets[e + 1]) - p0);
-    int nb0, nb1;
+    e = __builtin_amdgcn_readfirstlane(a.tiles[2 * mt]);
+    p0 = __builtin_amdgcn_readfirstlane(a.tiles[2 * mt + 1]);
+    rows_valid = min(BT, __builtin_amdgcn_readfirstlane(a.offsets[e + 1]) - p0);
     if (FC1) {
       nb0 = nt;                  // gate block
       nb1 = a.inter / 128 + nt;  // up block
@@ -234,42 +247,52 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
       nb0 = 2 * nt;
       nb1 = min(2 * nt + 1, nblk_w - 1);
     }
-
-    // ---- per-lane DMA sources -------------------------------------------
     // weights: the tile's K-blocks are contiguous 32 KB pieces
-    const uint8_t* a_src =
-        a.w + ((int64_t)e * a.n_tiles + nt) * kbs * (int64_t)C::A_BYTES + (wave * C::A_INSTR * 64 + lane) * 16;
-    auto src_row = [&](int t) -> int64_t {
-      const int p = p0 + min(t, rows_valid - 1);
-      if (!FC1) return p;
-      const int r = a.sorted_route[p];
-      return a.a_mode == 2 ? r : r / a.top_k;
-    };
+    a_src = a.w + ((int64_t)e * a.n_tiles + nt) * kbs * (int64_t)C::A_BYTES + (wave * C::A_INSTR * 64 + lane) * 16;
     // tokens: LDS position V (16 bytes) of the stage holds chunk
     // (V % 8) ^ tok_swz(token) of token V / 8 (see tok_swz)
-    const uint8_t* b_src[C::B_INSTR];
 #pragma unroll
     for (int j = 0; j < C::B_INSTR; ++j) {
-      const int v = wave * BT + j * 64 + (lane < C::B_LANES ? lane : 0);
-      const int t = v >> 3;
-      const int chunk = (v & 7) ^ tok_swz(t & 15);
+      const int v8 = wave * BT + j * 64 + (lane < C::B_LANES ? lane : 0);
+      const int t = v8 >> 3;
+      const int chunk = (v8 & 7) ^ tok_swz(t & 15);
       b_src[j] = a.a + src_row(t) * a.k_dim + chunk * 16;
     }
     // token scales: a stage carries those of the next K-block (the promotion
     // threads turn them into ratios one K-block ahead of their use)
-    const float* s_src = a.a_scale + src_row(wave * C::S_LANES + (lane < C::S_LANES ? lane : 0)) * kbs;
+    s_src = a.a_scale + src_row(wave * C::S_LANES + (lane < C::S_LANES ? lane : 0)) * kbs;
     // L2 prefetch of weights kPrefetchAhead K-blocks ahead of the stage
     // being loaded: the gm token tiles of a group share this weight tile
     // (they run side by side on one XCD), so each prefetches every gm-th of
     // its 256 lines; one word per line lands in l2sink.  Weight K-blocks are
     // first touches (the token rows are L2 hits by then), and a stage waits
     // for its slowest load.
-    const int pf_lanes = 32 / gm;  // lines per wave per K-block
+    pf_lanes = 32 / gm;  // lines per wave per K-block
     const int pf_line = (wave * pf_lanes + (lane < pf_lanes ? lane : 0)) * gm + (mt - m0);
-    const uint8_t* pf_src = a.w + ((int64_t)e * a.n_tiles + nt) * kbs * (int64_t)C::A_BYTES + pf_line * 128;
-    // once per tile: this tile's two weight-scale columns (waves 0-3) and the
-    // token scales of K-block 0; both are older than every stage load, so the
-    // first stage's wait covers them
+    pf_src = a.w + ((int64_t)e * a.n_tiles + nt) * kbs * (int64_t)C::A_BYTES + pf_line * 128;
+  };
+
+  auto issue = [&](auto stage, int kb) {
+    const lds_u8* As = ring(stage);
+    const lds_u8* Bs = As + C::A_BYTES;
+    const lds_u8* Ss = Bs + C::B_BYTES;
+#pragma unroll
+    for (int j = 0; j < C::A_INSTR; ++j)
+      dma16(a_src + (int64_t)kb * C::A_BYTES + j * 1024, As + (wave * C::A_INSTR + j) * 1024);
+#pragma unroll
+    for (int j = 0; j < C::B_INSTR; ++j)
+      if (lane < C::B_LANES) dma16(b_src[j] + kb * kKB, Bs + (wave * BT + j * 64) * 16);
+    if (lane < C::S_LANES) dma4(s_src + min(kb + 1, kbs - 1), Ss + wave * C::S_LANES * 4);
+    if (lane < pf_lanes)
+      dma4(reinterpret_cast<const float*>(pf_src + (int64_t)min(kb + kPrefetchAhead, kbs - 1) * C::A_BYTES),
+           (const lds_u8*)l2sink + wave * 256);
+  };
+
+  // The loads a tile needs before its first step: its two weight-scale
+  // columns (waves 0-3), the token scales of K-block 0 and the first
+  // STAGES - 1 stages.  The scale loads are older than every stage load, so
+  // the first stage's wait covers them.
+  auto prologue = [&]() {
     if (wave < 4) {
       const int blk = wave >> 1, half = wave & 1;
       const int kb = half * 64 + lane;
@@ -280,24 +303,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
     if (lane < C::S_LANES) dma4(s_src, (const lds_u8*)sx0 + wave * C::S_LANES * 4);
     // K-block 0 meets a zero accumulator: any finite ratio will do
     if (prole) rsc[0][pt][pb] = 0.0f;
+    issue(std::integral_constant<int, 0>{}, 0);
+    if (C::STAGES > 2 && 1 < kbs) issue(std::integral_constant<int, 1>{}, 1);
+    if (C::STAGES > 3 && 2 < kbs) issue(std::integral_constant<int, (C::STAGES > 3 ? 2 : 0)>{}, 2);
+  };
+
+  int64_t v = v_begin + slot;
+  if (v < v_end) {
+    setup(v);
+    prologue();
+  }
+  for (; v < v_end; v += per_xcd) {
     float pf = 1.0f;
-
-    auto issue = [&](auto stage, int kb) {
-      const lds_u8* As = ring(stage);
-      const lds_u8* Bs = As + C::A_BYTES;
-      const lds_u8* Ss = Bs + C::B_BYTES;
-#pragma unroll
-      for (int j = 0; j < C::A_INSTR; ++j)
-        dma16(a_src + (int64_t)kb * C::A_BYTES + j * 1024, As + (wave * C::A_INSTR + j) * 1024);
-#pragma unroll
-      for (int j = 0; j < C::B_INSTR; ++j)
-        if (lane < C::B_LANES) dma16(b_src[j] + kb * kKB, Bs + (wave * BT + j * 64) * 16);
-      if (lane < C::S_LANES) dma4(s_src + min(kb + 1, kbs - 1), Ss + wave * C::S_LANES * 4);
-      if (lane < pf_lanes)
-        dma4(reinterpret_cast<const float*>(pf_src + (int64_t)min(kb + kPrefetchAhead, kbs - 1) * C::A_BYTES),
-             (const lds_u8*)l2sink + wave * 256);
-    };
-
     v4f acc[C::NB][C::TBW];
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb)
@@ -389,9 +406,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
         }
       }
     };
-    issue(std::integral_constant<int, 0>{}, 0);
-    if (C::STAGES > 2 && 1 < kbs) issue(std::integral_constant<int, 1>{}, 1);
-    if (C::STAGES > 3 && 2 < kbs) issue(std::integral_constant<int, (C::STAGES > 3 ? 2 : 0)>{}, 2);
     for (int kb = 0; kb < kbs; kb += C::STAGES) {
       step(std::integral_constant<int, 0>{}, kb);
       if (kb + 1 < kbs) step(std::integral_constant<int, 1>{}, kb + 1);
@@ -400,6 +414,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
     }
     if (prole) fsc[pt][pb] = pf;
     __syncthreads();  // every wave is done with the ring (and fsc is visible) before the epilogue
+    // this tile's epilogue coordinates; then the next tile's first loads
+    const int ep_p0 = p0, ep_rows = rows_valid, ep_nt = nt;
+    if (v + per_xcd < v_end) {
+      setup(v + per_xcd);
+      prologue();
+    }
     // undo the running scale: acc = sum_kb F_kb * (block product)
 #pragma unroll
     for (int tb = 0; tb < C::TBW; ++tb) {
@@ -413,7 +433,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
       // h = silu(gate) * up = g / (1 + 2^(-g log2 e)) * up on the hardware
       // exp2 and reciprocal; then the 1x128 amax, s = amax / 448 and the
       // codes of h * (1 / s).
-      float* red = reinterpret_cast<float*>(smem);  // [WN][BT] partial amax
+      float* red = red_s;  // [WN][BT] partial amax
       float hv[C::TBW][C::NB / 2][4];
 #pragma unroll
       for (int tb = 0; tb < C::TBW; ++tb) {
@@ -431,7 +451,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
         m = fmaxf(m, __shfl_xor(m, 32));
         if (lane < 16) red[wn * BT + wt * C::TW + tb * 16 + lane] = m;
       }
-      __syncthreads();
+      // LDS-only exchange: a fenced barrier would also wait for the next
+      // tile's loads issued above
+      wait_lgkmcnt0();
+      barrier_nofence();
       const int ikb = a.inter / 128;
 #pragma unroll
       for (int tb = 0; tb < C::TBW; ++tb) {
@@ -441,19 +464,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
         for (int w = 0; w < C::WN; ++w) amax = fmaxf(amax, red[w * BT + t]);
         const float s = amax / kE4m3Max;
         const float inv = s != 0.f ? kE4m3Max * __builtin_amdgcn_rcpf(amax) : 0.f;
-        if (t < rows_valid) {
-          uint8_t* dst = a.hq + (int64_t)(p0 + t) * a.inter + nt * 128 + wn * C::G + 4 * (lane >> 4);
+        if (t < ep_rows) {
+          uint8_t* dst = a.hq + (int64_t)(ep_p0 + t) * a.inter + ep_nt * 128 + wn * C::G + 4 * (lane >> 4);
 #pragma unroll
           for (int g = 0; g < C::NB / 2; ++g) {
             int w = cvt2_e4m3(hv[tb][g][0] * inv, hv[tb][g][1] * inv, 0, false);
             w = cvt2_e4m3(hv[tb][g][2] * inv, hv[tb][g][3] * inv, w, true);
             *reinterpret_cast<uint32_t*>(dst + g * 16) = (uint32_t)w;
           }
-          if (wn == 0 && (lane >> 4) == 0) a.hs[(int64_t)(p0 + t) * ikb + nt] = s;
+          if (wn == 0 && (lane >> 4) == 0) a.hs[(int64_t)(ep_p0 + t) * ikb + ep_nt] = s;
         }
       }
     } else {
-      const int n0 = nt * kBN;
+      const int n0 = ep_nt * kBN;
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb) {
         const int n = (nb < C::NB / 2 ? wn * C::G + nb * 16 : 128 + wn * C::G + (nb - C::NB / 2) * 16) +
@@ -461,16 +484,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
 #pragma unroll
         for (int tb = 0; tb < C::TBW; ++tb) {
           const int t = wt * C::TW + tb * 16 + (lane & 15);
-          if (t < rows_valid && n0 + n < a.n_rows) {
+          if (t < ep_rows && n0 + n < a.n_rows) {
             u32x2 o;
             o[0] = f32_to_bf16_rne(acc[nb][tb][0]) | (f32_to_bf16_rne(acc[nb][tb][1]) << 16);
             o[1] = f32_to_bf16_rne(acc[nb][tb][2]) | (f32_to_bf16_rne(acc[nb][tb][3]) << 16);
-            *reinterpret_cast<u32x2*>(a.y + (int64_t)(p0 + t) * a.n_rows + n0 + n) = o;
+            *reinterpret_cast<u32x2*>(a.y + (int64_t)(ep_p0 + t) * a.n_rows + n0 + n) = o;
           }
         }
       }
     }
-    __syncthreads();  // the next tile's DMA reuses the LDS the epilogue read
   }
 }
 
