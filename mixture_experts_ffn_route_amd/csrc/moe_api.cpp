@@ -28,6 +28,7 @@ struct moe_layer {
   int32_t expected_m;
   float capacity_factor;
   int32_t staged_tokens;
+  bool compacted;  // the staging launch also compacted the routes (small batches)
   void* out;
   int32_t grid_fc1, grid_fc2;
   // profiling
@@ -68,6 +69,26 @@ int prof_begin(moe_layer* l, int kind, hipStream_t s) {
 
 void prof_end(moe_layer* l, int idx, hipStream_t s) {
   if (idx >= 0) (void)hipEventRecord(l->pending[idx].stop, s);
+}
+
+// Compaction arguments for the T tokens currently staged.
+moe::CompactArgs compact_args(moe_layer* l, int32_t T) {
+  moe::CompactArgs ca;
+  const int32_t routes = T * l->cfg.top_k;
+  ca.staged_idx = region<int32_t>(l, MOE_REGION_STAGED_IDX);
+  ca.routes = routes;
+  ca.num_experts = l->cfg.num_experts;
+  ca.row_cap = (int32_t)l->L.row_cap;
+  ca.block_m = l->tac.block_m;
+  ca.blocks = (routes + moe::kCompactChunk - 1) / moe::kCompactChunk;
+  ca.hdr = region<uint32_t>(l, MOE_REGION_STATUS);
+  ca.blk_base = region<int32_t>(l, moe::kRegionBlkBase);
+  ca.counts = region<int32_t>(l, MOE_REGION_COUNTS);
+  ca.offsets = region<int32_t>(l, MOE_REGION_OFFSETS);
+  ca.sorted_route = region<int32_t>(l, MOE_REGION_SORTED_ROUTE);
+  ca.route_pos = region<int32_t>(l, MOE_REGION_ROUTE_POS);
+  ca.tiles = region<int32_t>(l, MOE_REGION_TILES);
+  return ca;
 }
 
 moe_status_t hip_fail(const char* what) {
@@ -129,6 +150,7 @@ extern "C" moe_status_t moe_layer_create(const moe_config_t* cfg, int32_t expect
   l->expected_m = expected_m;
   l->capacity_factor = capacity_factor;
   l->staged_tokens = -1;
+  l->compacted = false;
   l->out = nullptr;
   const bool mx = cfg->weight_format == MOE_WEIGHT_MXFP8_E4M3;
   auto grid = [&](int which) {
@@ -204,9 +226,15 @@ extern "C" moe_status_t moe_stage_inputs(moe_layer_t* l, const void* x, const fl
   a.xs = region<float>(l, MOE_REGION_XS);
   a.x_plane = (int64_t)l->L.rows_x * l->cfg.hidden;
   a.xs_mx = region<uint32_t>(l, MOE_REGION_XS);
+  // Small batches (up to kFuseRoutes routes) stage and compact in one launch;
+  // the compaction is then one workgroup, which beyond that size costs more
+  // than the separate launches it saves.  Larger ones compact in the forward.
+  const bool fuse = (int64_t)num_tokens * l->cfg.top_k <= moe::kFuseRoutes;
   const int p = prof_begin(l, MOE_KERNEL_STAGE, s);
-  if (moe::launch_stage(a, stream) != 0) return hip_fail("stage launch");
+  const int rc = fuse ? moe::launch_stage_compact(a, compact_args(l, num_tokens), stream) : moe::launch_stage(a, stream);
+  if (rc != 0) return hip_fail("stage launch");
   prof_end(l, p, s);
+  l->compacted = fuse;
   l->staged_tokens = num_tokens;
   l->out = out_bf16;
   return MOE_OK;
@@ -219,25 +247,14 @@ extern "C" moe_status_t moe_layer_forward(moe_layer_t* l, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const moe_config_t& c = l->cfg;
   const int32_t T = l->staged_tokens;
-  const int32_t routes = T * c.top_k;
 
-  moe::CompactArgs ca;
-  ca.staged_idx = region<int32_t>(l, MOE_REGION_STAGED_IDX);
-  ca.routes = routes;
-  ca.num_experts = c.num_experts;
-  ca.row_cap = (int32_t)l->L.row_cap;
-  ca.block_m = l->tac.block_m;
-  ca.blocks = (routes + moe::kCompactChunk - 1) / moe::kCompactChunk;
-  ca.hdr = region<uint32_t>(l, MOE_REGION_STATUS);
-  ca.blk_base = region<int32_t>(l, moe::kRegionBlkBase);
-  ca.counts = region<int32_t>(l, MOE_REGION_COUNTS);
-  ca.offsets = region<int32_t>(l, MOE_REGION_OFFSETS);
-  ca.sorted_route = region<int32_t>(l, MOE_REGION_SORTED_ROUTE);
-  ca.route_pos = region<int32_t>(l, MOE_REGION_ROUTE_POS);
-  ca.tiles = region<int32_t>(l, MOE_REGION_TILES);
-  int p = prof_begin(l, MOE_KERNEL_COMPACT, s);
-  if (moe::launch_compact(ca, stream) != 0) return hip_fail("compact launch");
-  prof_end(l, p, s);
+  const moe::CompactArgs ca = compact_args(l, T);
+  int p = -1;
+  if (!l->compacted) {
+    p = prof_begin(l, MOE_KERNEL_COMPACT, s);
+    if (moe::launch_compact(ca, stream) != 0) return hip_fail("compact launch");
+    prof_end(l, p, s);
+  }
 
   if (c.weight_format == MOE_WEIGHT_MXFP8_E4M3) {
     moe::MxGemmArgs m1;

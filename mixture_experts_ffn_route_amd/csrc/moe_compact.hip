@@ -17,186 +17,16 @@
 // ranges in order and keep running per-expert counts in LDS.
 #include <hip/hip_runtime.h>
 
+#include "moe_compact_dev.h"
 #include "moe_device.h"
 #include "moe_internal.h"
 
 namespace moe {
 
-constexpr int kCompactThreads = 256;
-constexpr int kCompactWaves = kCompactThreads / 64;
-constexpr int kItems = kCompactChunk / kCompactThreads;  // routes per lane per block
-
-__device__ __forceinline__ int id_bits(int num_experts) {
-  int b = 0;
-  while ((1 << b) < num_experts) ++b;
-  return b;
-}
-
-// Lanes of this wave whose route has the same expert as this lane (valid lanes only).
-__device__ __forceinline__ uint64_t peers_of(int e, bool valid, int nbits) {
-  uint64_t m = __ballot(valid);
-  for (int b = 0; b < nbits; ++b) {
-    const bool bit = valid && ((e >> b) & 1);
-    const uint64_t bb = __ballot(bit);
-    m &= bit ? bb : ~bb;
-  }
-  return m;
-}
-
-// Walk this block's routes wave by wave.  hist[w*E + e] holds wave w's
-// running count; rank[i] receives the count of same-expert routes before
-// item i within this wave's range.
-__device__ void sweep(const CompactArgs& a, int blk, int* hist, int* rank, int* expert) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nbits = id_bits(a.num_experts);
-  const int64_t base = (int64_t)blk * kCompactChunk + (int64_t)wave * (kCompactChunk / kCompactWaves);
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-#pragma unroll
-  for (int it = 0; it < kItems; ++it) {
-    const int64_t r = base + it * 64 + lane;
-    const int e = r < a.routes ? a.staged_idx[r] : -1;
-    const bool valid = e >= 0;
-    const uint64_t pm = peers_of(e, valid, nbits);
-    const int below = __popcll(pm & lt);
-    int run = 0;
-    if (valid) run = hist[wave * a.num_experts + e];
-    rank[it] = run + below;
-    expert[it] = e;
-    if (valid && below == 0) hist[wave * a.num_experts + e] = run + __popcll(pm);
-  }
-}
-
-__device__ void clear_hist(int* hist, int n) {
-  for (int i = threadIdx.x; i < n; i += kCompactThreads) hist[i] = 0;
-}
-
-// Exclusive prefix sum of v[0..n) in place (n <= 1024) by wave 0; returns the total.
-__device__ int wave0_exclusive_scan(int* v, int n, int* total_out) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    const int per = (n + 63) / 64;
-    int s = 0;
-    for (int i = 0; i < per; ++i) {
-      const int j = lane * per + i;
-      if (j < n) s += v[j];
-    }
-    int incl = s;
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += o;
-    }
-    int run = incl - s;
-    for (int i = 0; i < per; ++i) {
-      const int j = lane * per + i;
-      if (j < n) {
-        const int c = v[j];
-        v[j] = run;
-        run += c;
-      }
-    }
-    if (lane == 63) *total_out = incl;
-  }
-  __syncthreads();
-  return *total_out;
-}
-
-// From full per-expert counts in `cnt` (LDS, E entries): kept counts/offsets,
-// capacity flag, route total and the tile list.  `tmp` is LDS scratch of E+1.
-__device__ void finish_counts(const CompactArgs& a, int* cnt, int* tmp, int* scalar) {
-  const int E = a.num_experts;
-  // full exclusive offsets -> tmp
-  for (int e = threadIdx.x; e < E; e += kCompactThreads) tmp[e] = cnt[e];
-  __syncthreads();
-  const int total = wave0_exclusive_scan(tmp, E, scalar);
-  const int cap = a.row_cap;
-  for (int e = threadIdx.x; e < E; e += kCompactThreads) {
-    const int lo = min(tmp[e], cap);
-    const int hi = min(tmp[e] + cnt[e], cap);
-    a.offsets[e] = lo;
-    a.counts[e] = hi - lo;
-  }
-  if (threadIdx.x == 0) {
-    a.offsets[E] = min(total, cap);
-    a.hdr[kHdrRoutes] = (uint32_t)min(total, cap);
-    if (total > cap) atomicOr(a.hdr + kHdrStatus, (uint32_t)MOE_DEV_CAPACITY);
-  }
-  __syncthreads();
-  // tiles per expert (kept rows), scanned into cnt (reused)
-  for (int e = threadIdx.x; e < E; e += kCompactThreads) {
-    const int lo = min(tmp[e], cap), hi = min(tmp[e] + cnt[e], cap);
-    cnt[e] = (hi - lo + a.block_m - 1) / a.block_m;
-  }
-  __syncthreads();
-  // keep the full offsets in tmp; scan tiles in cnt
-  const int ntiles = wave0_exclusive_scan(cnt, E, scalar + 1);
-  for (int e = threadIdx.x; e < E; e += kCompactThreads) {
-    const int lo = min(tmp[e], cap);
-    const int kept_hi = (e + 1 < E) ? min(tmp[e + 1], cap) : min(total, cap);
-    int m = cnt[e];
-    for (int p = lo; p < kept_hi; p += a.block_m, ++m) {
-      a.tiles[2 * m] = e;
-      a.tiles[2 * m + 1] = p;
-    }
-  }
-  if (threadIdx.x == 0) a.hdr[kHdrMTiles] = (uint32_t)ntiles;
-}
-
-// Positions from the per-wave running ranks; wave bases come from
-// blk_base (this block's first position per expert) plus earlier waves.
-__device__ void scatter(const CompactArgs& a, int blk, int* hist, const int* blk_start, const int* rank,
-                        const int* expert) {
-  const int E = a.num_experts;
-  for (int e = threadIdx.x; e < E; e += kCompactThreads) {
-    int run = blk_start[e];
-    for (int w = 0; w < kCompactWaves; ++w) {
-      const int c = hist[w * E + e];
-      hist[w * E + e] = run;
-      run += c;
-    }
-  }
-  __syncthreads();
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t base = (int64_t)blk * kCompactChunk + (int64_t)wave * (kCompactChunk / kCompactWaves);
-#pragma unroll
-  for (int it = 0; it < kItems; ++it) {
-    const int64_t r = base + it * 64 + lane;
-    if (r >= a.routes) continue;
-    const int e = expert[it];
-    int p = -1;
-    if (e >= 0) {
-      p = hist[wave * E + e] + rank[it];
-      if (p < a.row_cap) {
-        a.sorted_route[p] = (int)r;
-      } else {
-        p = -1;
-      }
-    }
-    a.route_pos[r] = p;
-  }
-}
-
 // Single-workgroup path (routes <= kCompactChunk): count, scan, scatter.
 __global__ __launch_bounds__(kCompactThreads) void compact_fused_kernel(CompactArgs a) {
   extern __shared__ int lds[];
-  const int E = a.num_experts;
-  int* hist = lds;                        // [waves, E]
-  int* cnt = hist + kCompactWaves * E;    // [E]
-  int* tmp = cnt + E;                     // [E + 1]
-  int* scalar = tmp + E + 1;              // [2]
-  int rank[kItems], expert[kItems];
-  clear_hist(hist, kCompactWaves * E);
-  __syncthreads();
-  sweep(a, 0, hist, rank, expert);
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kCompactThreads) {
-    int s = 0;
-    for (int w = 0; w < kCompactWaves; ++w) s += hist[w * E + e];
-    cnt[e] = s;
-  }
-  __syncthreads();
-  finish_counts(a, cnt, tmp, scalar);
-  __syncthreads();
-  scatter(a, 0, hist, tmp, rank, expert);  // tmp holds the full exclusive offsets
+  compact_one_workgroup(a, lds);
 }
 
 // Multi-workgroup path, kernel 1: per-block per-expert counts -> blk_base.
@@ -258,8 +88,7 @@ int launch_compact(const CompactArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int E = a.num_experts;
   if (a.blocks <= 1) {
-    const size_t lds = (size_t)(kCompactWaves * E + E + E + 1 + 2) * 4;
-    hipLaunchKernelGGL(compact_fused_kernel, dim3(1), dim3(kCompactThreads), lds, s, a);
+    hipLaunchKernelGGL(compact_fused_kernel, dim3(1), dim3(kCompactThreads), compact_one_workgroup_lds(E), s, a);
   } else {
     const size_t lds_hist = (size_t)(kCompactWaves * E + E) * 4;
     const size_t lds_scan = (size_t)(E + E + 1 + 2) * 4;

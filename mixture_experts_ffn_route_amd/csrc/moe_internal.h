@@ -11,6 +11,7 @@ namespace moe {
 
 constexpr int kMaxExperts = 1024;
 constexpr int kCompactChunk = 4096;  // routes per compaction workgroup (256 lanes x 16)
+constexpr int kFuseRoutes = 2048;    // staging and compaction share one launch up to this many routes
 constexpr int kNumRegions = 18;
 constexpr int kRegionBlkBase = 17;   // internal: per-(compaction block, expert) bases
 
@@ -87,6 +88,8 @@ struct CompactArgs {
   int32_t* tiles;          // [max_m_tiles, 2]
 };
 int launch_compact(const CompactArgs& a, void* stream);
+// Stage and compact in one launch (routes <= kCompactChunk).
+int launch_stage_compact(const StageArgs& a, const CompactArgs& c, void* stream);
 
 struct GemmArgs {
   // A operand: activation rows

@@ -6,6 +6,7 @@
 // touching the caller's tensors).
 #include <hip/hip_runtime.h>
 
+#include "moe_compact_dev.h"
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -15,9 +16,7 @@ namespace moe {
 //   s = amax / 448 (IEEE float division), q = RNE_sat(x / s), s == 0 -> q = 0.
 // With a prequantised input (x_scale != null) codes and scales are copied.
 // Block 0 also resets the device header for this batch.
-__global__ __launch_bounds__(256) void stage_quant_kernel(StageArgs a, int64_t groups, int copies) {
-  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (blockIdx.x == 0 && threadIdx.x < 64) a.hdr[threadIdx.x] = threadIdx.x == kHdrTokens ? (uint32_t)a.tokens : 0u;
+__device__ inline void quant_1x128(const StageArgs& a, int64_t g, int64_t groups, int copies) {
   const int64_t grp = g >> 4;
   if (grp >= groups) return;
   const int lane16 = threadIdx.x & 15;
@@ -68,9 +67,7 @@ __global__ __launch_bounds__(256) void stage_quant_kernel(StageArgs a, int64_t g
 // Four lanes per 32-column block, eight columns each.  Writes the hi codes
 // to plane 0, the lo codes to plane 1 (x_plane bytes further) and one word
 // (e_hi + 127) | (e_lo + 127) << 8 per block.  Block 0 resets the header.
-__global__ __launch_bounds__(256) void stage_split_kernel(StageArgs a, int64_t groups) {
-  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (blockIdx.x == 0 && threadIdx.x < 64) a.hdr[threadIdx.x] = threadIdx.x == kHdrTokens ? (uint32_t)a.tokens : 0u;
+__device__ inline void split_mx(const StageArgs& a, int64_t g, int64_t groups) {
   const int64_t grp = g >> 2;
   if (grp >= groups) return;
   const int q = a.hidden >> 5;
@@ -103,9 +100,7 @@ __global__ __launch_bounds__(256) void stage_split_kernel(StageArgs a, int64_t g
 
 // One thread per token slot row in [0, max_rows).  Live rows are checked and
 // masked; rows past the live count are staged as masked.
-__global__ __launch_bounds__(256) void stage_routes_kernel(StageArgs a) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= a.max_rows) return;
+__device__ inline void stage_route_row(const StageArgs& a, int t) {
   const int K = a.top_k;
   uint32_t bits = 0;
   int ids[8];
@@ -168,20 +163,76 @@ __global__ __launch_bounds__(256) void stage_routes_kernel(StageArgs a) {
   if (bits) atomicOr(a.hdr + kHdrStatus, bits);
 }
 
+__device__ inline void reset_header(const StageArgs& a) {
+  if (threadIdx.x < 64) a.hdr[threadIdx.x] = threadIdx.x == kHdrTokens ? (uint32_t)a.tokens : 0u;
+}
+
+__global__ __launch_bounds__(256) void stage_quant_kernel(StageArgs a, int64_t groups, int copies) {
+  if (blockIdx.x == 0) reset_header(a);
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (a.act_format == MOE_ACT_BF16)
+    split_mx(a, g, groups);
+  else
+    quant_1x128(a, g, groups, copies);
+}
+
+// One thread per token slot row in [0, max_rows).  Runs after the header reset
+// of stage_quant_kernel (same stream).
+__global__ __launch_bounds__(256) void stage_routes_kernel(StageArgs a) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t < a.max_rows) stage_route_row(a, t);
+}
+
+// Small batches (routes <= kCompactChunk): one launch stages everything.
+// Blocks [0, quant_blocks) quantise (or split) x; the last block resets the
+// header, stages and checks every route row, then compacts the routes as a
+// single workgroup, so the forward starts at FC1.
+__global__ __launch_bounds__(256) void stage_fused_kernel(StageArgs a, CompactArgs c, int64_t groups, int copies,
+                                                          int quant_blocks) {
+  extern __shared__ int lds[];
+  if ((int)blockIdx.x < quant_blocks) {
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (a.act_format == MOE_ACT_BF16)
+      split_mx(a, g, groups);
+    else
+      quant_1x128(a, g, groups, copies);
+    return;
+  }
+  reset_header(a);
+  __syncthreads();
+  for (int t = threadIdx.x; t < a.max_rows; t += 256) stage_route_row(a, t);
+  __syncthreads();  // this workgroup's route stores are visible to its own loads
+  compact_one_workgroup(c, lds);
+}
+
+static void quant_grid(const StageArgs& a, int64_t* groups, int* blocks, int* copies) {
+  if (a.act_format == MOE_ACT_BF16) {
+    *groups = (int64_t)a.tokens * (a.hidden / 32);
+    *blocks = (int)((*groups * 4 + 255) / 256);
+  } else {
+    *groups = (int64_t)a.tokens * (a.hidden / 128);
+    *blocks = (int)((*groups * 16 + 255) / 256);
+  }
+  *copies = (a.flags & MOE_FLAG_PER_ROUTE_STAGING) ? a.top_k : 1;
+}
+
 int launch_stage(const StageArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (a.act_format == MOE_ACT_BF16) {
-    const int64_t groups = (int64_t)a.tokens * (a.hidden / 32);
-    const int qblocks = (int)((groups * 4 + 255) / 256);
-    hipLaunchKernelGGL(stage_split_kernel, dim3(qblocks > 0 ? qblocks : 1), dim3(256), 0, s, a, groups);
-  } else {
-    const int64_t groups = (int64_t)a.tokens * (a.hidden / 128);
-    const int64_t threads = groups * 16;
-    const int qblocks = (int)((threads + 255) / 256);
-    const int copies = (a.flags & MOE_FLAG_PER_ROUTE_STAGING) ? a.top_k : 1;
-    hipLaunchKernelGGL(stage_quant_kernel, dim3(qblocks > 0 ? qblocks : 1), dim3(256), 0, s, a, groups, copies);
-  }
+  int64_t groups;
+  int qblocks, copies;
+  quant_grid(a, &groups, &qblocks, &copies);
+  hipLaunchKernelGGL(stage_quant_kernel, dim3(qblocks > 0 ? qblocks : 1), dim3(256), 0, s, a, groups, copies);
   hipLaunchKernelGGL(stage_routes_kernel, dim3((a.max_rows + 255) / 256), dim3(256), 0, s, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_stage_compact(const StageArgs& a, const CompactArgs& c, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int64_t groups;
+  int qblocks, copies;
+  quant_grid(a, &groups, &qblocks, &copies);
+  hipLaunchKernelGGL(stage_fused_kernel, dim3(qblocks + 1), dim3(256), compact_one_workgroup_lds(c.num_experts), s, a,
+                     c, groups, copies, qblocks);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
