@@ -107,9 +107,12 @@ def run_cpu_baseline(inp, sample_tokens):
     from oracle import moe_ref
 
     S = sample_tokens
-    fwd = moe_ref.forward_mx if inp.weight_format == "mxfp8" else moe_ref.forward_fp8
     t0 = time.perf_counter()
-    fwd(inp.x_bf16[:S], inp.topk_idx[:S], inp.topk_w[:S], inp.w13, inp.w13_scale, inp.w2, inp.w2_scale)
+    args = (inp.x_bf16[:S], inp.topk_idx[:S], inp.topk_w[:S], inp.w13, inp.w13_scale, inp.w2, inp.w2_scale)
+    if inp.weight_format.startswith("mxfp8"):
+        moe_ref.forward_mx(*args, elem="e5m2" if inp.weight_format == "mxfp8_e5m2" else "e4m3")
+    else:
+        moe_ref.forward_fp8(*args)
     dt = time.perf_counter() - t0
     R = S * inp.shape.top_k
     flops = 6.0 * R * inp.shape.hidden * inp.shape.intermediate
@@ -127,9 +130,9 @@ def main():
     ap.add_argument("--config", default="dsv3", choices=["tiny", "small", "dsv3", "skewed"])
     ap.add_argument("--tokens", type=int, default=None, help="override T (token sweep)")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--weights", default="fp8_block", choices=["fp8_block", "mxfp8"],
+    ap.add_argument("--weights", default="fp8_block", choices=["fp8_block", "mxfp8", "mxfp8_e5m2"],
                     help="fp8_block: e4m3 + 128x128 scales, e4m3 1x128 activations; "
-                         "mxfp8: e4m3 + E8M0 per 32 weights x BF16 activations")
+                         "mxfp8 / mxfp8_e5m2: e4m3 / e5m2 + E8M0 per 32 weights x BF16 activations")
     ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens for the CPU oracle baseline (0: skip)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (reference for HBM byte counters)")
@@ -150,7 +153,7 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     base = CONFIGS[args.config]
-    mx = args.weights == "mxfp8"
+    mx = ("e5m2" if args.weights == "mxfp8_e5m2" else "e4m3") if args.weights.startswith("mxfp8") else False
     # The MXFP8 x BF16 path issues two FP8 MFMAs per K-block (hi and lo
     # activation terms), so its ceiling in layer FLOPs is half the FP8 peak.
     peak = FP8_PEAK_TFLOPS / 2 if mx else FP8_PEAK_TFLOPS
@@ -231,7 +234,7 @@ def main():
         log(f"[bench] cpu baseline {cpu}")
 
     workload = (f"{args.config} T={T} H={H} I={I} E={shape.experts} K={shape.top_k} routing={shape.routing}"
-                + (" weights=mxfp8 activations=bf16" if mx else ""))
+                + (f" weights=mxfp8_{mx} activations=bf16" if mx else ""))
     line = {
         "metric": METRIC,
         "value": round(flops / sec / 1e12, 3),
@@ -243,7 +246,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 x mxfp8_e4m3" if mx else "fp8_e4m3",
+        "dtype": f"bf16 x mxfp8_{mx}" if mx else "fp8_e4m3",
         "data": "synthetic",
         "config": {"workload": workload, "tokens": T, "routes": R,
                    "hbm_gbs_algorithmic": round(B / sec / 1e9, 1),

@@ -58,7 +58,10 @@ enum {
   MOE_WEIGHT_E4M3_BLOCK128 = 0,
   /* e4m3 codes with one E8M0 exponent per 32 consecutive K elements (OCP MX)
    * -- the MXFP8 weights of PR #4604. */
-  MOE_WEIGHT_MXFP8_E4M3 = 1
+  MOE_WEIGHT_MXFP8_E4M3 = 1,
+  /* e5m2 (OCP, max 57344) codes with one E8M0 exponent per 32 consecutive K
+   * elements -- the other MXFP8 element type of PR #4604. */
+  MOE_WEIGHT_MXFP8_E5M2 = 2
 };
 
 /* Activation formats (what moe_stage_inputs receives and FC1 consumes). */
@@ -83,7 +86,13 @@ enum {
   /* Stage one activation row per route instead of one per token.  Exists to
    * show the deduplicated layout gives identical results (PR #4069,
    * Description, deduplicated dispatch bullet); costs K times the rows. */
-  MOE_FLAG_PER_ROUTE_STAGING = 2u
+  MOE_FLAG_PER_ROUTE_STAGING = 2u,
+  /* Unfused FC1 (E4M3_BLOCK128 weights only): the FC1 GEMM stores its FP32
+   * gate/up output in MOE_REGION_GATEUP and a separate kernel applies SwiGLU
+   * and the 1x128 requantisation.  A debug and cross-check path for the fused
+   * epilogue (PR #4069, Description: the fused FC1 reproduces the unfused
+   * path); it gives the same bits and costs a 2I x 4-byte row per route. */
+  MOE_FLAG_UNFUSED_FC1 = 4u
 };
 
 /* Device status bits (moe_read_status). */
@@ -108,7 +117,7 @@ typedef struct {
  *   w13       e4m3 [E, 2I, H]   rows 0..I-1 gate, rows I..2I-1 up
  *   w2        e4m3 [E, H, I]
  *   E4M3_BLOCK128: w13_scale float32 [E, 2I/128, H/128], w2_scale float32 [E, H/128, I/128]
- *   MXFP8_E4M3:    w13_scale uint8   [E, 2I, H/32],      w2_scale uint8   [E, H, I/32]
+ *   MXFP8_E4M3 / MXFP8_E5M2: w13_scale uint8 [E, 2I, H/32], w2_scale uint8 [E, H, I/32]
  * The caller keeps them alive and unchanged while the layer handle exists. */
 typedef struct {
   const void* w13;
@@ -148,7 +157,8 @@ enum {
   MOE_REGION_W13T = 13,         /* e4m3 w13 tiled at create: [E, I/128, H/128] tiles of 32 KB */
   MOE_REGION_W2T = 14,          /* e4m3 w2 tiled at create: [E, ceil(H/256), I/128] tiles of 32 KB */
   MOE_REGION_W13S = 15,         /* MXFP8: w13 E8M0 tiled at create, 1 KB per w13 tile (empty for FP8) */
-  MOE_REGION_W2S = 16           /* MXFP8: w2 E8M0 tiled at create, 1 KB per w2 tile (empty for FP8) */
+  MOE_REGION_W2S = 16,          /* MXFP8: w2 E8M0 tiled at create, 1 KB per w2 tile (empty for FP8) */
+  MOE_REGION_GATEUP = 17        /* MOE_FLAG_UNFUSED_FC1: float32 [row_cap, 2I] gate then up columns (else empty) */
 };
 
 /* Kernel classes timed by the optional profiler. */

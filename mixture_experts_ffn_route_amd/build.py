@@ -29,6 +29,7 @@ SOURCES = [
     "moe_compact.hip",
     "moe_gemm_fp8.hip",
     "moe_gemm_mx.hip",
+    "moe_swiglu.hip",
     "moe_combine.hip",
     "moe_weights.hip",
 ]

@@ -152,7 +152,7 @@ extern "C" moe_status_t moe_layer_create(const moe_config_t* cfg, int32_t expect
   l->staged_tokens = -1;
   l->compacted = false;
   l->out = nullptr;
-  const bool mx = cfg->weight_format == MOE_WEIGHT_MXFP8_E4M3;
+  const bool mx = moe::is_mx(cfg->weight_format);
   auto grid = [&](int which) {
     int g = cus * (mx ? moe::gemm_mx_max_workgroups_per_cu(which, t.block_m)
                       : moe::gemm_max_workgroups_per_cu(which, t.block_m));
@@ -256,7 +256,7 @@ extern "C" moe_status_t moe_layer_forward(moe_layer_t* l, void* stream) {
     prof_end(l, p, s);
   }
 
-  if (c.weight_format == MOE_WEIGHT_MXFP8_E4M3) {
+  if (moe::is_mx(c.weight_format)) {
     moe::MxGemmArgs m1;
     memset(&m1, 0, sizeof(m1));
     m1.a = region<uint8_t>(l, MOE_REGION_XQ);
@@ -278,6 +278,7 @@ extern "C" moe_status_t moe_layer_forward(moe_layer_t* l, void* stream) {
     m1.h_plane = l->L.row_cap * c.intermediate;
     m1.hs = region<uint32_t>(l, MOE_REGION_HS);
     m1.grid = l->grid_fc1;
+    m1.w_e5m2 = c.weight_format == MOE_WEIGHT_MXFP8_E5M2;
     p = prof_begin(l, MOE_KERNEL_FC1, s);
     if (moe::launch_fc1_mx(m1, l->tac.block_m, stream) != 0) return hip_fail("fc1 launch");
     prof_end(l, p, s);
@@ -301,6 +302,7 @@ extern "C" moe_status_t moe_layer_forward(moe_layer_t* l, void* stream) {
     m2.hdr = ca.hdr;
     m2.y = region<uint16_t>(l, MOE_REGION_Y);
     m2.grid = l->grid_fc2;
+    m2.w_e5m2 = m1.w_e5m2;
     p = prof_begin(l, MOE_KERNEL_FC2, s);
     if (moe::launch_fc2_mx(m2, l->tac.block_m, stream) != 0) return hip_fail("fc2 launch");
     prof_end(l, p, s);
@@ -326,8 +328,13 @@ extern "C" moe_status_t moe_layer_forward(moe_layer_t* l, void* stream) {
   g1.hq = region<uint8_t>(l, MOE_REGION_HQ);
   g1.hs = region<float>(l, MOE_REGION_HS);
   g1.grid = l->grid_fc1;
+  const bool unfused = (c.flags & MOE_FLAG_UNFUSED_FC1) != 0;
+  g1.gateup = unfused ? region<float>(l, MOE_REGION_GATEUP) : nullptr;
   p = prof_begin(l, MOE_KERNEL_FC1, s);
   if (moe::launch_fc1(g1, l->tac.block_m, stream) != 0) return hip_fail("fc1 launch");
+  if (unfused && moe::launch_swiglu_quant(g1.gateup, (int32_t)l->L.row_cap, c.intermediate, g1.hdr, g1.hq, g1.hs,
+                                          stream) != 0)
+    return hip_fail("swiglu launch");
   prof_end(l, p, s);
 
   moe::GemmArgs g2;
@@ -370,7 +377,7 @@ extern "C" moe_status_t moe_read_status(moe_layer_t* l, void* stream, uint32_t* 
 extern "C" moe_status_t moe_layer_region(moe_layer_t* l, int32_t r, void** dptr, size_t* bytes) {
   moe::clear_error();
   if (!l || !dptr || !bytes) return moe::fail(MOE_ERR_INVALID_ARG, "NULL argument");
-  if (r < 0 || r > MOE_REGION_W2S) return moe::fail(MOE_ERR_INVALID_ARG, "unknown region %d", r);
+  if (r < 0 || r > MOE_REGION_GATEUP) return moe::fail(MOE_ERR_INVALID_ARG, "unknown region %d", r);
   *dptr = l->ws + l->L.off[r];
   *bytes = l->L.size[r];
   return MOE_OK;
@@ -386,7 +393,7 @@ extern "C" moe_status_t moe_layer_tactic(const moe_layer_t* l, moe_tactic_t* t) 
   t->grid_fc2 = l->grid_fc2;
   t->row_cap = (int32_t)l->L.row_cap;
   t->max_m_tiles = (int32_t)l->L.max_m_tiles;
-  t->tile_order = l->cfg.weight_format == MOE_WEIGHT_MXFP8_E4M3 ? moe::kTileOrderMx : moe::kTileOrder16;
+  t->tile_order = moe::is_mx(l->cfg.weight_format) ? moe::kTileOrderMx : moe::kTileOrder16;
   return MOE_OK;
 }
 

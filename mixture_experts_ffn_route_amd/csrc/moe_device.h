@@ -60,6 +60,19 @@ __device__ __forceinline__ uint32_t mx_term4(const float v[4], int e, float r[4]
   return u;
 }
 
+// SwiGLU of one (gate, up) pair: silu(g) * u = g / (1 + 2^(-g log2 e)) * u on
+// the hardware exp2 and reciprocal.  The fused FC1 epilogue and the unfused
+// SwiGLU kernel both use this, so the two paths give the same bits.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.44269504f)) * u;
+}
+
+// 1x128 requantisation factor: codes are RNE_sat(h * inv) with
+// inv = 448 / amax, and 0 when the block's scale s = amax / 448 is 0.
+__device__ __forceinline__ float requant_inv(float amax, float s) {
+  return s != 0.f ? kE4m3Max * __builtin_amdgcn_rcpf(amax) : 0.f;
+}
+
 // Maximum over groups of `width` consecutive lanes (width a power of two <= 64).
 template <int WIDTH>
 __device__ __forceinline__ float group_max(float v) {

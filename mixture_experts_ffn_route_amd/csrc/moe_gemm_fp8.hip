@@ -429,7 +429,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
     }
 
     // ---- epilogue -----------------------------------------------------------
-    if (FC1) {
+    if (FC1 && a.gateup != nullptr) {
+      // unfused FC1: FP32 gate and up rows, SwiGLU + requant run separately
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) {
+        const int col = (nb < C::NB / 2 ? 0 : a.inter) + ep_nt * 128 + wn * C::G + (nb % (C::NB / 2)) * 16 + 4 * (lane >> 4);
+#pragma unroll
+        for (int tb = 0; tb < C::TBW; ++tb) {
+          const int t = wt * C::TW + tb * 16 + (lane & 15);
+          if (t < ep_rows) *reinterpret_cast<v4f*>(a.gateup + (int64_t)(ep_p0 + t) * (2 * a.inter) + col) = acc[nb][tb];
+        }
+      }
+    } else if (FC1) {
       // h = silu(gate) * up = g / (1 + 2^(-g log2 e)) * up on the hardware
       // exp2 and reciprocal; then the 1x128 amax, s = amax / 448 and the
       // codes of h * (1 / s).
@@ -443,7 +454,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float gt = acc[g][tb][i], up = acc[C::NB / 2 + g][tb][i];
-            const float h = gt * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gt * 1.44269504f)) * up;
+            const float h = swiglu(gt, up);
             hv[tb][g][i] = h;
             m = fmaxf(m, fabsf(h));
           }
@@ -463,7 +474,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
 #pragma unroll
         for (int w = 0; w < C::WN; ++w) amax = fmaxf(amax, red[w * BT + t]);
         const float s = amax / kE4m3Max;
-        const float inv = s != 0.f ? kE4m3Max * __builtin_amdgcn_rcpf(amax) : 0.f;
+        const float inv = requant_inv(amax, s);
         if (t < ep_rows) {
           uint8_t* dst = a.hq + (int64_t)(ep_p0 + t) * a.inter + ep_nt * 128 + wn * C::G + 4 * (lane >> 4);
 #pragma unroll

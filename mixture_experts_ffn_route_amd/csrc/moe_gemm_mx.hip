@@ -1,7 +1,7 @@
 // MXFP8-weight x BF16-activation grouped GEMMs of the MoE layer on gfx950
 // MX-scaled MFMA (the variant of "feat(moe_ep): MXFP8 x BF16 integration",
-// flashinfer PR #4604, Description: e4m3 weights with one E8M0 exponent per
-// 32 K-elements, BF16 activations, BF16 h between the GEMMs).
+// flashinfer PR #4604, Description: e4m3 or e5m2 weights with one E8M0
+// exponent per 32 K-elements, BF16 activations, BF16 h between the GEMMs).
 //
 // FC1: gu[p, n] = sum_k x[t, k] * w13[e, n, k] * 2^(s13[e, n, k/32] - 127)
 //      h = bf16_RNE(silu(gate) * up)
@@ -49,11 +49,12 @@ typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) const uint32_t lds_u32;
 
 // Scaled MFMA: A = weights (row operand), B = activation term (column
-// operand).  OA / OB pick the byte of the scale words: lane l's scale word
-// supplies the exponent of row (or column) l%16 for 32-block l/16.
-template <int OA, int OB>
+// operand, always e4m3).  FA is the weight element type (0 e4m3, 1 e5m2).
+// OA / OB pick the byte of the scale words: lane l's scale word supplies the
+// exponent of row (or column) l%16 for 32-block l/16.
+template <int FA, int OA, int OB>
 __device__ __forceinline__ v4f mfma_mx(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, OA, sa, OB, sb);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, 0, OA, sa, OB, sb);
 }
 
 __device__ __forceinline__ v8i lds_frag(const lds_u8* p) {
@@ -115,7 +116,7 @@ struct MxCfg {
   static_assert(2 * 8 * BT * 4 <= STAGE, "epilogue scratch fits in ring stage 0");
 };
 
-template <int BT, bool FC1>
+template <int BT, bool FC1, int FA>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
   using C = MxCfg<BT>;
   __shared__ __attribute__((aligned(1024))) uint8_t ring0[C::STAGE];
@@ -245,8 +246,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
         const int sa = nb < C::NBH ? sa_g : sa_u;
 #pragma unroll
         for (int tb = 0; tb < C::TBW; ++tb) {
-          acc[nb][tb] = mfma_mx<OA, 0>(aq, bh[tb], acc[nb][tb], sa, sb[tb]);
-          acc[nb][tb] = mfma_mx<OA, 1>(aq, bl[tb], acc[nb][tb], sa, sb[tb]);
+          acc[nb][tb] = mfma_mx<FA, OA, 0>(aq, bh[tb], acc[nb][tb], sa, sb[tb]);
+          acc[nb][tb] = mfma_mx<FA, OA, 1>(aq, bl[tb], acc[nb][tb], sa, sb[tb]);
         }
         __builtin_amdgcn_sched_barrier(0);
         aq = an;
@@ -354,8 +355,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
 
 template <int BT, bool FC1>
 int launch_one(const MxGemmArgs& a, void* stream) {
-  hipLaunchKernelGGL((gemm_mx_kernel<BT, FC1>), dim3(a.grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
-                     a);
+  if (a.w_e5m2)
+    hipLaunchKernelGGL((gemm_mx_kernel<BT, FC1, 1>), dim3(a.grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                       a);
+  else
+    hipLaunchKernelGGL((gemm_mx_kernel<BT, FC1, 0>), dim3(a.grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                       a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -373,7 +378,7 @@ int launch_bt(const MxGemmArgs& a, int block_m, void* stream) {
 template <int BT, bool FC1>
 int occ() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_mx_kernel<BT, FC1>, kThreads, 0) != hipSuccess) return 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_mx_kernel<BT, FC1, 0>, kThreads, 0) != hipSuccess) return 1;
   return n > 0 ? n : 1;
 }
 

@@ -51,16 +51,16 @@ moe_status_t validate_config(const moe_config_t* cfg, int32_t expected_m, int32_
     return fail(MOE_ERR_UNSUPPORTED, "top_k %d not in {1, 2, 4, 6, 8}", cfg->top_k);
   if (cfg->top_k > cfg->num_experts)
     return fail(MOE_ERR_INVALID_ARG, "top_k %d exceeds num_experts %d", cfg->top_k, cfg->num_experts);
-  if (cfg->flags & ~(uint32_t)(MOE_FLAG_CHECK_ROUTES | MOE_FLAG_PER_ROUTE_STAGING))
+  if (cfg->flags & ~(uint32_t)(MOE_FLAG_CHECK_ROUTES | MOE_FLAG_PER_ROUTE_STAGING | MOE_FLAG_UNFUSED_FC1))
     return fail(MOE_ERR_INVALID_ARG, "unknown flag bits 0x%x", cfg->flags);
   if (cfg->weight_format == MOE_WEIGHT_E4M3_BLOCK128) {
     if (cfg->act_format != MOE_ACT_E4M3_1X128)
       return fail(MOE_ERR_UNSUPPORTED, "E4M3_BLOCK128 weights need E4M3_1X128 activations");
-  } else if (cfg->weight_format == MOE_WEIGHT_MXFP8_E4M3) {
+  } else if (is_mx(cfg->weight_format)) {
     if (cfg->act_format != MOE_ACT_BF16)
       return fail(MOE_ERR_UNSUPPORTED, "MXFP8 weights need BF16 activations");
-    if (cfg->flags & MOE_FLAG_PER_ROUTE_STAGING)
-      return fail(MOE_ERR_UNSUPPORTED, "per-route staging is only provided for the FP8 path");
+    if (cfg->flags & (MOE_FLAG_PER_ROUTE_STAGING | MOE_FLAG_UNFUSED_FC1))
+      return fail(MOE_ERR_UNSUPPORTED, "per-route staging and the unfused FC1 are only provided for the FP8 path");
   } else {
     return fail(MOE_ERR_INVALID_ARG, "unknown weight_format %d", cfg->weight_format);
   }
@@ -83,10 +83,10 @@ Tactic choose_tactic(const moe_config_t& cfg, int32_t expected_m) {
   Tactic t;
   t.bucket = token_bucket(expected_m);
   t.block_n = 256;
-  const int cap = cfg.weight_format == MOE_WEIGHT_MXFP8_E4M3 ? 128 : 256;
+  const int cap = is_mx(cfg.weight_format) ? 128 : 256;
   t.block_m = t.bucket <= 16 ? 16 : (t.bucket >= cap ? cap : t.bucket);
   t.stages = t.block_m >= 256 ? 2 : (t.block_m >= 64 ? 3 : 4);
-  if (cfg.weight_format == MOE_WEIGHT_MXFP8_E4M3) t.stages = t.block_m >= 128 ? 2 : (t.block_m >= 32 ? 3 : 4);
+  if (is_mx(cfg.weight_format)) t.stages = t.block_m >= 128 ? 2 : (t.block_m >= 32 ? 3 : 4);
   return t;
 }
 
@@ -124,6 +124,7 @@ Layout compute_layout(const moe_config_t& cfg, const Tactic& t, int32_t max_rows
   // MX: one 1 KB exponent tile per 32 KB code tile
   L.size[MOE_REGION_W13S] = mx ? L.size[MOE_REGION_W13T] / 32 : 0;
   L.size[MOE_REGION_W2S] = mx ? L.size[MOE_REGION_W2T] / 32 : 0;
+  L.size[MOE_REGION_GATEUP] = (cfg.flags & MOE_FLAG_UNFUSED_FC1) ? L.row_cap * 2 * I * 4 : 0;
   L.size[kRegionBlkBase] = L.compact_blocks * E * 4;
   size_t off = 0;
   for (int r = 0; r < kNumRegions; ++r) {

@@ -12,8 +12,8 @@ namespace moe {
 constexpr int kMaxExperts = 1024;
 constexpr int kCompactChunk = 4096;  // routes per compaction workgroup (256 lanes x 16)
 constexpr int kFuseRoutes = 2048;    // staging and compaction share one launch up to this many routes
-constexpr int kNumRegions = 18;
-constexpr int kRegionBlkBase = 17;   // internal: per-(compaction block, expert) bases
+constexpr int kNumRegions = 19;
+constexpr int kRegionBlkBase = 18;   // internal: per-(compaction block, expert) bases
 
 // Words of the device header (MOE_REGION_STATUS).
 enum HeaderWord : int {
@@ -112,9 +112,13 @@ struct GemmArgs {
   // outputs
   uint8_t* hq;  float* hs; // FC1: e4m3 [R, I], scales [R, I/128]
   uint16_t* y;             // FC2: bf16 [R, H]
+  float* gateup;           // FC1, unfused: FP32 gate/up rows [R, 2I] instead of the fused epilogue
   int32_t grid;
 };
 int launch_fc1(const GemmArgs& a, int block_m, void* stream);
+// Unfused FC1 second half: SwiGLU + 1x128 requant of the FP32 gate/up rows.
+int launch_swiglu_quant(const float* gateup, int32_t row_cap, int32_t inter, const uint32_t* hdr, uint8_t* hq,
+                        float* hs, void* stream);
 int launch_fc2(const GemmArgs& a, int block_m, void* stream);
 int gemm_max_workgroups_per_cu(int which, int block_m);
 
@@ -138,6 +142,7 @@ struct MxGemmArgs {
   uint32_t* hs;              // FC1: packed E8M0 [R, I/32]
   uint16_t* y;               // FC2: bf16 [R, H]
   int32_t grid;
+  int32_t w_e5m2;            // weight element type: 0 e4m3, 1 e5m2
 };
 int launch_fc1_mx(const MxGemmArgs& a, int block_m, void* stream);
 int launch_fc2_mx(const MxGemmArgs& a, int block_m, void* stream);
@@ -151,6 +156,11 @@ struct CombineArgs {
   uint16_t* out;
 };
 int launch_combine(const CombineArgs& a, void* stream);
+
+// MXFP8 weight formats (either element type, E8M0 scales per 32).
+inline bool is_mx(int weight_format) {
+  return weight_format == MOE_WEIGHT_MXFP8_E4M3 || weight_format == MOE_WEIGHT_MXFP8_E5M2;
+}
 
 // Weight tile orders (moe_weights.hip): 16x16x128 fragments (FP8 path) and
 // the MX-scaled operand order (MXFP8 path).

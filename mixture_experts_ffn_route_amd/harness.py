@@ -36,12 +36,13 @@ def to_device(inp, device="cuda") -> DeviceInputs:
 
 
 def make_layer(shape, dev: DeviceInputs, *, expected_m: Optional[int] = None, max_rows: Optional[int] = None,
-               capacity_factor: float = 1.0, flags: int = L.MOE_FLAG_CHECK_ROUTES, mx: bool = False) -> MoELayer:
-    """``mx``: MXFP8 weights (E8M0 per 32) with BF16 activations, else FP8 block-scale."""
+               capacity_factor: float = 1.0, flags: int = L.MOE_FLAG_CHECK_ROUTES, mx=False) -> MoELayer:
+    """``mx``: MXFP8 weights (E8M0 per 32) with BF16 activations, else FP8 block-scale;
+    ``mx="e5m2"`` selects e5m2 weight codes, any other true value e4m3."""
     T = shape.tokens
     if expected_m is None:
         expected_m = max(1, T * shape.top_k // shape.experts)
-    wf = L.MOE_WEIGHT_MXFP8_E4M3 if mx else L.MOE_WEIGHT_E4M3_BLOCK128
+    wf = (L.MOE_WEIGHT_MXFP8_E5M2 if mx == "e5m2" else L.MOE_WEIGHT_MXFP8_E4M3) if mx else L.MOE_WEIGHT_E4M3_BLOCK128
     af = L.MOE_ACT_BF16 if mx else L.MOE_ACT_E4M3_1X128
     return MoELayer(shape.hidden, shape.intermediate, shape.experts, shape.top_k, dev.w13, dev.w13_scale, dev.w2,
                     dev.w2_scale, expected_m=expected_m, max_rows=max_rows or max(T, 1),

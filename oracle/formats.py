@@ -7,6 +7,9 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
   path in "feat(moe_ep): add SM90 push FP8 mega-MoE backend for Hopper"
   (Description: FC1 with fused SwiGLU + 1x128 quantization) and the MXFP8
   weights of "feat(moe_ep): MXFP8 x BF16 integration" (Description).
+* OCP 8-bit floating point E5M2 (IEEE-like: exponent field 31 is inf or NaN,
+  largest finite magnitude 57344) -- the second MXFP8 element type of
+  "feat(moe_ep): MXFP8 x BF16 integration" (Description).
 * OCP MX E8M0 shared scale: value 2**(v - 127), v = 255 is NaN.
 * bfloat16: 1 sign, 8 exponent, 7 mantissa bits (the layer's output type).
 
@@ -42,6 +45,28 @@ def e4m3_decode(codes) -> np.ndarray:
     fields and looked up.)
     """
     return _E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def _e5m2_fields(c: np.ndarray) -> np.ndarray:
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 2) & 0x1F
+    m = c & 0x3
+    mag = np.where(e == 0, (m / 4.0) * 2.0 ** -14, (1.0 + m / 4.0) * np.exp2(e - 15.0))
+    mag = np.where(e == 31, np.where(m == 0, np.inf, np.nan), mag)
+    return sign * mag
+
+
+_E5M2_TABLE = _e5m2_fields(np.arange(256, dtype=np.int64))
+
+
+def e5m2_decode(codes) -> np.ndarray:
+    """Decode e5m2 codes (uint8) to float64 from the bit fields.
+
+    sign = bit 7, exponent field e = bits 6..2 (bias 15), mantissa m = bits 1..0.
+    e == 0: subnormal (m / 4) * 2**-14; e == 31: +-inf (m == 0) or NaN;
+    otherwise (1 + m / 4) * 2**(e - 15).
+    """
+    return _E5M2_TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
 def e8m0_decode(codes) -> np.ndarray:

@@ -57,6 +57,7 @@ from .formats import (
     bf16_bits_to_f64,
     bf16_rne_bits,
     e4m3_decode,
+    e5m2_decode,
     e4m3_encode_rne_sat,
     e8m0_decode,
 )
@@ -99,10 +100,12 @@ def dequant_rows_1x128(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return e4m3_decode(codes) * s
 
 
-def dequant_mx(codes: np.ndarray, e8m0: np.ndarray) -> np.ndarray:
-    """e4m3 codes [N, K] with one E8M0 scale per 32 consecutive K elements."""
+def dequant_mx(codes: np.ndarray, e8m0: np.ndarray, elem: str = "e4m3") -> np.ndarray:
+    """MXFP8 codes [N, K] (elem "e4m3" or "e5m2") with one E8M0 scale per 32
+    consecutive K elements."""
     s = np.repeat(e8m0_decode(e8m0), 32, axis=1)
-    return e4m3_decode(codes) * s
+    dec = e5m2_decode if elem == "e5m2" else e4m3_decode
+    return dec(codes) * s
 
 
 def silu(z: np.ndarray) -> np.ndarray:
@@ -350,8 +353,8 @@ def _combine_dict(yd: dict, route_pos, staged_w, top_k, token_ids, hdim):
 
 def forward_mx(x_bf16_bits, topk_idx, topk_w, w13, w13_e8m0, w2, w2_e8m0, *,
                row_cap: Optional[int] = None, check_routes: bool = True,
-               token_ids: Optional[np.ndarray] = None) -> ForwardResult:
-    """BF16 activations x MXFP8 (e4m3 + E8M0 per 32 along K) weights.
+               token_ids: Optional[np.ndarray] = None, elem: str = "e4m3") -> ForwardResult:
+    """BF16 activations x MXFP8 (e4m3 or e5m2 codes + E8M0 per 32 along K) weights.
 
     Same pipeline as ``forward_fp8`` except: activations are used as exact
     BF16 values (no quantisation), weights are decoded with their E8M0
@@ -372,12 +375,12 @@ def forward_mx(x_bf16_bits, topk_idx, topk_w, w13, w13_e8m0, w2, w2_e8m0, *,
         if pos.size == 0:
             continue
         toks = comp.sorted_route[pos] // top_k
-        w = dequant_mx(w13[e], w13_e8m0[e])
+        w = dequant_mx(w13[e], w13_e8m0[e], elem)
         gu = x[toks] @ w.T
         i = w.shape[0] // 2
         h = silu(gu[:, :i]) * gu[:, i:]
         hbits = bf16_rne_bits(h)
-        ye = bf16_bits_to_f64(hbits) @ dequant_mx(w2[e], w2_e8m0[e]).T
+        ye = bf16_bits_to_f64(hbits) @ dequant_mx(w2[e], w2_e8m0[e], elem).T
         for j, p in enumerate(pos):
             hb[int(p)], yd[int(p)] = hbits[j], ye[j]
     tid = np.arange(tokens) if token_ids is None else np.asarray(token_ids)

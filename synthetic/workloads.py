@@ -15,12 +15,13 @@ can be regenerated alone):
   ``W2``, one sub-stream per expert);
 * weights stored either as e4m3 codes with one float32 scale per 128x128 block
   (scale = amax/448, the DeepSeek-style block scaling the SM90 push backend
-  page lists among its supported configurations), or as e4m3 codes with one
-  E8M0 exponent per 32 consecutive K elements (the OCP MX v1.0 rule used by the
-  MXFP8 x BF16 MegaMoE integration page).
+  page lists among its supported configurations), or as e4m3 or e5m2 codes
+  with one E8M0 exponent per 32 consecutive K elements (the OCP MX v1.0 rule
+  used by the MXFP8 x BF16 MegaMoE integration page).
 
-The float8 encodings are done by torch's ``float8_e4m3fn`` cast after clamping
-to +-448; nothing here re-implements the layer's quantisers.
+The float8 encodings are done by torch's ``float8_e4m3fn`` / ``float8_e5m2``
+casts after clamping to the format's largest finite value; nothing here
+re-implements the layer's quantisers.
 """
 
 from __future__ import annotations
@@ -38,6 +39,7 @@ import torch
 ROUTER, X, W13, W2, MASK = 1, 2, 3, 4, 5
 
 E4M3_MAX = 448.0
+E5M2_MAX = 57344.0
 
 
 @dataclass(frozen=True)
@@ -179,15 +181,28 @@ def _block_quant_one(w: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     return _e4m3_codes(v.reshape(n, k)), scale
 
 
-def _mx_quant_one(w: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+def _e5m2_codes(v: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.clip(v, -E5M2_MAX, E5M2_MAX))
+    return t.to(torch.float8_e5m2).view(torch.uint8).numpy()
+
+
+def _mx_quant_one(w: np.ndarray, elem: str = "e4m3") -> Tuple[np.ndarray, np.ndarray]:
+    """OCP MX v1.0: shared exponent floor(log2 amax_32) - emax(elem), elements
+    cast to the element type (emax 8 for e4m3, 15 for e5m2)."""
     n, k = w.shape
     blk = w.reshape(n, k // 32, 32)
     amax = np.abs(blk).max(axis=2)
     _, ex = np.frexp(amax)  # amax = m * 2**ex, m in [0.5, 1)
-    shared = np.where(amax > 0, ex.astype(np.int32) - 1 - 8, -127)  # floor(log2 amax) - emax(e4m3)
+    emax = 15 if elem == "e5m2" else 8
+    shared = np.where(amax > 0, ex.astype(np.int32) - 1 - emax, -127)
     shared = np.clip(shared, -127, 127).astype(np.int32)
     v = np.ldexp(blk, -shared[:, :, None]).astype(np.float32)
-    return _e4m3_codes(v.reshape(n, k)), (shared + 127).astype(np.uint8)
+    codes = _e5m2_codes(v.reshape(n, k)) if elem == "e5m2" else _e4m3_codes(v.reshape(n, k))
+    return codes, (shared + 127).astype(np.uint8)
+
+
+def _mx_quant_one_e5m2(w: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    return _mx_quant_one(w, "e5m2")
 
 
 def _per_expert(fn, seed, stream, experts, rows, cols, hidden):
@@ -209,15 +224,17 @@ def make_fp8_block_weights(experts: int, rows: int, cols: int, hidden: int, seed
     return _per_expert(_block_quant_one, seed, stream, experts, rows, cols, hidden)
 
 
-def make_mxfp8_weights(experts: int, rows: int, cols: int, hidden: int, seed: int, stream: int):
-    """e4m3 codes ``uint8 [E, rows, cols]`` + E8M0 exponents ``uint8 [E, rows, cols/32]``."""
-    return _per_expert(_mx_quant_one, seed, stream, experts, rows, cols, hidden)
+def make_mxfp8_weights(experts: int, rows: int, cols: int, hidden: int, seed: int, stream: int,
+                       elem: str = "e4m3"):
+    """e4m3 (or e5m2) codes ``uint8 [E, rows, cols]`` + E8M0 exponents ``uint8 [E, rows, cols/32]``."""
+    fn = _mx_quant_one_e5m2 if elem == "e5m2" else _mx_quant_one
+    return _per_expert(fn, seed, stream, experts, rows, cols, hidden)
 
 
 @dataclass
 class LayerInputs:
     shape: MoEShape
-    weight_format: str  # "fp8_block" | "mxfp8"
+    weight_format: str  # "fp8_block" | "mxfp8" | "mxfp8_e5m2"
     x_bf16: np.ndarray  # uint16 [T, H]
     topk_idx: np.ndarray  # int32 [T, K]
     topk_w: np.ndarray  # float32 [T, K]
@@ -235,9 +252,13 @@ def make_layer_inputs(shape: MoEShape, seed: int = 0, weight_format: str = "fp8_
     T, H, I, E = shape.tokens, shape.hidden, shape.intermediate, shape.experts
     idx, w = make_routing(shape, seed, masked_fraction=masked_fraction)
     x = make_activations(T, H, seed)
-    maker = make_fp8_block_weights if weight_format == "fp8_block" else make_mxfp8_weights
-    if weight_format not in ("fp8_block", "mxfp8"):
+    if weight_format not in ("fp8_block", "mxfp8", "mxfp8_e5m2"):
         raise ValueError(weight_format)
+    if weight_format == "fp8_block":
+        maker = make_fp8_block_weights
+    else:
+        elem = "e5m2" if weight_format == "mxfp8_e5m2" else "e4m3"
+        maker = lambda *a: make_mxfp8_weights(*a, elem=elem)  # noqa: E731
     w13, s13 = maker(E, 2 * I, H, H, seed, W13)
     w2, s2 = maker(E, H, I, H, seed, W2)
     return LayerInputs(shape, weight_format, x, idx, w, w13, s13, w2, s2)

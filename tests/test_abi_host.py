@@ -149,3 +149,15 @@ def test_query_mx_variant_sizes():
              + R * (I // 32) * 4 - R * (I // 128) * 4
              + E * 2 * I * H // 32 + E * H * I // 32)  # weight exponent tiles
     assert abs((mx - fp8) - extra) <= 8 * 256  # region alignment only
+
+
+def test_unfused_fc1_flag():
+    """MOE_FLAG_UNFUSED_FC1 is an FP8-path debug mode: it adds an FP32 [row_cap, 2I]
+    gate/up region and is refused for MXFP8 weights."""
+    base = L.moe_workspace_query(_cfg(), 128, 4096, 1.0)
+    unf = L.moe_workspace_query(_cfg(flags=L.MOE_FLAG_CHECK_ROUTES | L.MOE_FLAG_UNFUSED_FC1), 128, 4096, 1.0)
+    assert abs((unf - base) - 4096 * 8 * 2 * 2048 * 4) <= 256
+    with pytest.raises(L.MoEError) as ei:
+        L.moe_workspace_query(_cfg(weight_format=L.MOE_WEIGHT_MXFP8_E4M3, act_format=L.MOE_ACT_BF16,
+                                   flags=L.MOE_FLAG_UNFUSED_FC1), 128, 4096, 1.0)
+    assert ei.value.status == L.MOE_ERR_UNSUPPORTED

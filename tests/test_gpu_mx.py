@@ -33,20 +33,25 @@ def _bits(out):
     return _np(out.view(torch.int16)).view(np.uint16)
 
 
-def _mx_inputs(shape, seed, **kw):
-    return make_layer_inputs(shape, seed=seed, weight_format="mxfp8", **kw)
+def _mx_inputs(shape, seed, elem="e4m3", **kw):
+    return make_layer_inputs(shape, seed=seed, weight_format="mxfp8_e5m2" if elem == "e5m2" else "mxfp8", **kw)
+
+
+def _elem(inp):
+    return "e5m2" if inp.weight_format == "mxfp8_e5m2" else "e4m3"
 
 
 def _gpu_run(inp, shape, **kw):
     dev = to_device(inp)
-    layer = make_layer(shape, dev, mx=True, **kw)
+    layer = make_layer(shape, dev, mx=_elem(inp), **kw)
     out = run_forward(layer, dev)
     torch.cuda.synchronize()
     return layer, dev, out
 
 
 def _oracle(inp, **kw):
-    return M.forward_mx(inp.x_bf16, inp.topk_idx, inp.topk_w, inp.w13, inp.w13_scale, inp.w2, inp.w2_scale, **kw)
+    return M.forward_mx(inp.x_bf16, inp.topk_idx, inp.topk_w, inp.w13, inp.w13_scale, inp.w2, inp.w2_scale,
+                        elem=_elem(inp), **kw)
 
 
 def _check_compaction(layer, res, shape, T):
@@ -81,15 +86,16 @@ def _check_split(x, hi, lo, e_hi, label):
     assert np.all((scaled >= 128) & (scaled < 256)), f"{label}: hi exponent does not map the block max into [128, 256)"
 
 
+@pytest.mark.parametrize("elem", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("cfg,masked", [("tiny", 0.0), ("tiny", 0.25), ("small", 0.0), ("small", 0.1)])
-def test_mx_layer_parity(cfg, masked):
+def test_mx_layer_parity(cfg, masked, elem):
     shape = CONFIGS[cfg]
-    inp = _mx_inputs(shape, 0, masked_fraction=masked)
+    inp = _mx_inputs(shape, 0, elem, masked_fraction=masked)
     layer, dev, out = _gpu_run(inp, shape)
     res = _oracle(inp)
     assert layer.status() == res.status == 0
     _check_compaction(layer, res, shape, shape.tokens)
-    assert_output_close(_bits(out), res.out_bits, f"mx {cfg} masked={masked}")
+    assert_output_close(_bits(out), res.out_bits, f"mx {elem} {cfg} masked={masked}")
 
 
 def test_mx_activation_split_bounds():
@@ -127,28 +133,29 @@ def test_mx_h_split_matches_bf16_h():
     assert np.all(np.abs(got - want) <= 0.02 * np.abs(want) + 0.01 * np.repeat(scale, 32, axis=1) + 1e-30)
 
 
+@pytest.mark.parametrize("elem", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("expected_m", [2, 12, 48, 4096])
-def test_mx_tactics_agree_bit_exact(expected_m):
+def test_mx_tactics_agree_bit_exact(expected_m, elem):
     shape = CONFIGS["small"]
-    inp = _mx_inputs(shape, 3)
+    inp = _mx_inputs(shape, 3, elem)
     dev = to_device(inp)
     outs = []
     for em in (expected_m, 96):
-        layer = make_layer(shape, dev, expected_m=em, mx=True)
+        layer = make_layer(shape, dev, expected_m=em, mx=elem)
         outs.append(_bits(run_forward(layer, dev)))
     assert np.array_equal(outs[0], outs[1])
 
 
-@pytest.mark.parametrize("tokens", [0, 1, 37, 301])
-def test_mx_ragged_token_counts(tokens):
+@pytest.mark.parametrize("tokens,elem", [(0, "e4m3"), (1, "e4m3"), (37, "e5m2"), (301, "e4m3"), (301, "e5m2")])
+def test_mx_ragged_token_counts(tokens, elem):
     shape = MoEShape(512, 2048, 768, 32, 6, "topk")
-    inp = _mx_inputs(shape, 4)
+    inp = _mx_inputs(shape, 4, elem)
     dev = to_device(inp)
-    layer = make_layer(shape, dev, expected_m=48, max_rows=512, mx=True)
+    layer = make_layer(shape, dev, expected_m=48, max_rows=512, mx=elem)
     out = run_forward(layer, dev, tokens=tokens)
     torch.cuda.synchronize()
     res = M.forward_mx(inp.x_bf16[:tokens], inp.topk_idx[:tokens], inp.topk_w[:tokens], inp.w13, inp.w13_scale,
-                       inp.w2, inp.w2_scale)
+                       inp.w2, inp.w2_scale, elem=elem)
     _check_compaction(layer, res, shape, tokens)
     if tokens:
         assert_output_close(_bits(out), res.out_bits, f"mx T={tokens}")
@@ -197,11 +204,12 @@ def _retile_mx_scales(s, fc1, inter):
     return out.reshape(-1)
 
 
-@pytest.mark.parametrize("shape", [CONFIGS["tiny"], MoEShape(16, 384, 256, 4, 2, "topk")])
-def test_mx_create_time_tiling_is_exact(shape):
-    inp = _mx_inputs(shape, 8)
+@pytest.mark.parametrize("shape,elem", [(CONFIGS["tiny"], "e4m3"), (MoEShape(16, 384, 256, 4, 2, "topk"), "e4m3"),
+                                        (MoEShape(16, 384, 256, 4, 2, "topk"), "e5m2")])
+def test_mx_create_time_tiling_is_exact(shape, elem):
+    inp = _mx_inputs(shape, 8, elem)
     dev = to_device(inp)
-    layer = make_layer(shape, dev, mx=True)
+    layer = make_layer(shape, dev, mx=elem)
     torch.cuda.synchronize()
     I = shape.intermediate
     assert np.array_equal(_np(layer.region("w13t", torch.uint8)), _retile_mx(inp.w13, True, I))
@@ -228,3 +236,17 @@ def test_mx_skewed_zipf_sampled():
     assert_output_close(_bits(out)[tok], res.out_bits, "mx zipf T=8192")
     full = _bits(out)
     assert np.all((full & 0x7F80) != 0x7F80)
+
+
+@pytest.mark.slow
+def test_mx_e5m2_dsv3_sampled():
+    """DSV3-like shape, T=4096, balanced routing, MXFP8 E5M2 weights x BF16."""
+    shape = CONFIGS["dsv3"]
+    inp = _mx_inputs(shape, 1, "e5m2")
+    layer, dev, out = _gpu_run(inp, shape)
+    rng = np.random.default_rng(1)
+    tok = np.sort(rng.choice(shape.tokens, size=16, replace=False))
+    res = _oracle(inp, token_ids=tok)
+    assert layer.status() == 0
+    _check_compaction(layer, res, shape, shape.tokens)
+    assert_output_close(_bits(out)[tok], res.out_bits, "mx e5m2 dsv3 T=4096")

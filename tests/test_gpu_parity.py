@@ -267,3 +267,40 @@ def test_create_time_weight_tiling_is_exact(shape, expected_m):
     torch.cuda.synchronize()
     res = M.forward_fp8(inp.x_bf16, inp.topk_idx, inp.topk_w, inp.w13, inp.w13_scale, inp.w2, inp.w2_scale)
     assert_output_close(_bits(run), res.out_bits, f"H={shape.hidden}")
+
+
+@pytest.mark.parametrize("cfg,expected_m", [("tiny", None), ("small", None), ("small", 4096)])
+def test_unfused_fc1_equals_fused(cfg, expected_m):
+    """The unfused FC1 (FP32 gate/up rows, then a separate SwiGLU + 1x128
+    requant kernel) gives the fused epilogue's codes, scales and output bit
+    for bit, and its gate/up rows match the oracle's FC1 GEMM alone."""
+    shape = CONFIGS[cfg]
+    inp = make_layer_inputs(shape, seed=11)
+    dev = to_device(inp)
+    fused = make_layer(shape, dev, expected_m=expected_m)
+    a = _bits(run_forward(fused, dev))
+    unf = make_layer(shape, dev, expected_m=expected_m, flags=L.MOE_FLAG_CHECK_ROUTES | L.MOE_FLAG_UNFUSED_FC1)
+    b = _bits(run_forward(unf, dev))
+    torch.cuda.synchronize()
+    I, H = shape.intermediate, shape.hidden
+    R = int(_np(fused.region("offsets", torch.int32, (shape.experts + 1,)))[-1])
+    assert np.array_equal(_np(fused.region("hq", torch.uint8))[:R * I], _np(unf.region("hq", torch.uint8))[:R * I])
+    assert np.array_equal(_np(fused.region("hs", torch.int32))[:R * I // 128],
+                          _np(unf.region("hs", torch.int32))[:R * I // 128])
+    assert np.array_equal(a, b)
+    # gate/up rows against the float64 GEMM of the staged rows
+    res = M.forward_fp8(inp.x_bf16, inp.topk_idx, inp.topk_w, inp.w13, inp.w13_scale, inp.w2, inp.w2_scale)
+    gu = _np(unf.region("gateup", torch.float32))[:R * 2 * I].reshape(R, 2 * I).astype(np.float64)
+    xd = M.dequant_rows_1x128(res.xq, res.xs)
+    offs = res.comp.offsets
+    for e in range(shape.experts):
+        lo, hi = offs[e], offs[e + 1]
+        if hi == lo:
+            continue
+        toks = res.comp.sorted_route[lo:hi] // shape.top_k
+        want = M.fc1_gateup(xd[toks], inp.w13[e], inp.w13_scale[e])
+        # FP32 accumulation of exact FP8 products (inside the MFMA and across
+        # K-blocks): ~2e-5 of the row maximum is observed; index or scale
+        # mistakes give O(1) errors
+        err = np.abs(gu[lo:hi] - want)
+        assert np.all(err <= 1e-4 * np.abs(want).max(axis=1, keepdims=True) + 1e-30), f"expert {e}: {err.max():.3e}"

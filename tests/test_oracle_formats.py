@@ -162,3 +162,29 @@ def test_bf16_overflow_and_subnormals():
     assert got[3] == 0.0  # tie to even (zero)
     assert got[4] == 2.0 ** -133
     assert got[5] == 0.0 and np.signbit(got[5])
+
+
+def test_e5m2_decode_exhaustive_vs_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = F.e5m2_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e5m2).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert set(np.nonzero(nan)[0].tolist()) == {0x7D, 0x7E, 0x7F, 0xFD, 0xFE, 0xFF}
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))
+
+
+def test_e5m2_decode_spec_values():
+    # tests/golden/e5m2_spec_values.txt: code -> value fixed by the OCP FP8 E5M2 definition
+    with open(f"{GOLDEN}/e5m2_spec_values.txt") as f:
+        rows = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+    for code, val in rows:
+        got = F.e5m2_decode(np.array([int(code, 16)], np.uint8))[0]
+        if val == "nan":
+            assert math.isnan(got)
+        elif val in ("inf", "-inf"):
+            assert got == float(val)
+        else:
+            assert got == float(Fraction(val)), (code, val, got)
+            assert math.copysign(1.0, got) == (-1.0 if val.startswith("-") else 1.0)
