@@ -133,6 +133,8 @@ def main():
     ap.add_argument("--weights", default="fp8_block", choices=["fp8_block", "mxfp8", "mxfp8_e5m2"],
                     help="fp8_block: e4m3 + 128x128 scales, e4m3 1x128 activations; "
                          "mxfp8 / mxfp8_e5m2: e4m3 / e5m2 + E8M0 per 32 weights x BF16 activations")
+    ap.add_argument("--combine", default="separate", choices=["separate", "fused"],
+                    help="separate: combine kernel after FC2; fused: last-arriver combine inside FC2")
     ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens for the CPU oracle baseline (0: skip)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (reference for HBM byte counters)")
@@ -157,6 +159,8 @@ def main():
     # The MXFP8 x BF16 path issues two FP8 MFMAs per K-block (hi and lo
     # activation terms), so its ceiling in layer FLOPs is half the FP8 peak.
     peak = FP8_PEAK_TFLOPS / 2 if mx else FP8_PEAK_TFLOPS
+    from mixture_experts_ffn_route_amd import _lib as L
+    flags = L.MOE_FLAG_CHECK_ROUTES | (L.MOE_FLAG_FUSED_COMBINE if args.combine == "fused" else 0)
 
     def measure(tokens, steps, warmup):
         shape = MoEShape(tokens, base.hidden, base.intermediate, base.experts, base.top_k, base.routing)
@@ -164,7 +168,7 @@ def main():
         inp = make_layer_inputs(shape, seed=args.seed, weight_format=args.weights)
         log(f"[bench] generated T={tokens} inputs in {time.perf_counter() - t0:.1f}s")
         dev = to_device(inp)
-        layer = make_layer(shape, dev, mx=mx)
+        layer = make_layer(shape, dev, mx=mx, flags=flags)
         out = torch.empty((tokens, shape.hidden), dtype=torch.bfloat16, device="cuda")
 
         def step():
@@ -194,7 +198,8 @@ def main():
         B = workload_bytes(shape, counts, T, mx=mx)
         kern = {k: v[0] / max(v[1], 1) for k, v in prof.items()}
         rec = {"tokens": T, "ms_per_step": sec * 1e3, "tflops": flops / sec / 1e12, "gbs": B / sec / 1e9,
-               "pct_mfma_peak": 100 * flops / sec / 1e12 / peak, "weights": args.weights, "pct_hbm_peak": 100 * B / sec / 1e9 / HBM_PEAK_GBS,
+               "pct_mfma_peak": 100 * flops / sec / 1e12 / peak, "weights": args.weights, "combine": args.combine,
+               "pct_hbm_peak": 100 * B / sec / 1e9 / HBM_PEAK_GBS,
                "kernel_ms": kern, "tactic": layer.tactic(), "status": status}
         log("[sweep]", json.dumps(rec))
         os.makedirs(os.path.dirname(args.sweep_out) or ".", exist_ok=True)
@@ -248,7 +253,7 @@ def main():
         "vs_baseline": None,
         "dtype": f"bf16 x mxfp8_{mx}" if mx else "fp8_e4m3",
         "data": "synthetic",
-        "config": {"workload": workload, "tokens": T, "routes": R,
+        "config": {"workload": workload, "tokens": T, "routes": R, "combine": args.combine,
                    "hbm_gbs_algorithmic": round(B / sec / 1e9, 1),
                    "pct_mfma_peak": round(100 * flops / sec / 1e12 / peak, 2),
                    "kernel_avg_ms": kern},

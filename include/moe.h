@@ -92,7 +92,19 @@ enum {
    * and the 1x128 requantisation.  A debug and cross-check path for the fused
    * epilogue (PR #4069, Description: the fused FC1 reproduces the unfused
    * path); it gives the same bits and costs a 2I x 4-byte row per route. */
-  MOE_FLAG_UNFUSED_FC1 = 4u
+  MOE_FLAG_UNFUSED_FC1 = 4u,
+  /* Fused last-arriver combine: FC2 still stores the un-weighted rows in
+   * MOE_REGION_Y, and the FC2 tile that stores the last kept route of a
+   * token over a 256-column slice reduces that token's routes over the slice
+   * into the output, with the standalone combine's FP32 arithmetic (same
+   * bits), so no combine launch follows FC2 (SM90 pull-style MegaMoE,
+   * flashinfer PR #4688, commit list: grouped token-back, where the last FC2
+   * row of a token's group reduces every member in FP32).  Uses the arrival
+   * counters of MOE_REGION_ARRIVE, zeroed at create and returned to zero by
+   * every forward.  The y rows are then stored write-through so that a tile
+   * on another XCD can read them; on MI355X this costs more than the
+   * separate combine launch it saves, so the flag is off by default. */
+  MOE_FLAG_FUSED_COMBINE = 8u
 };
 
 /* Device status bits (moe_read_status). */
@@ -158,7 +170,9 @@ enum {
   MOE_REGION_W2T = 14,          /* e4m3 w2 tiled at create: [E, ceil(H/256), I/128] tiles of 32 KB */
   MOE_REGION_W13S = 15,         /* MXFP8: w13 E8M0 tiled at create, 1 KB per w13 tile (empty for FP8) */
   MOE_REGION_W2S = 16,          /* MXFP8: w2 E8M0 tiled at create, 1 KB per w2 tile (empty for FP8) */
-  MOE_REGION_GATEUP = 17        /* MOE_FLAG_UNFUSED_FC1: float32 [row_cap, 2I] gate then up columns (else empty) */
+  MOE_REGION_GATEUP = 17,       /* MOE_FLAG_UNFUSED_FC1: float32 [row_cap, 2I] gate then up columns (else empty) */
+  MOE_REGION_ARRIVE = 18        /* MOE_FLAG_FUSED_COMBINE: int32 [max_rows, ceil(H/256)] arrival counters,
+                                   zero between forwards (else empty) */
 };
 
 /* Kernel classes timed by the optional profiler. */
@@ -220,7 +234,8 @@ moe_status_t moe_stage_inputs(moe_layer_t* layer, const void* x, const float* x_
                               const int32_t* topk_idx, const float* topk_w, int32_t num_tokens,
                               void* out_bf16, void* stream);
 
-/* Run compact -> FC1(+SwiGLU+requant) -> FC2 -> combine on the staged batch.
+/* Run compact -> FC1(+SwiGLU+requant) -> FC2 -> combine on the staged batch
+ * (with MOE_FLAG_FUSED_COMBINE the combine runs inside FC2).
  * Stream-ordered, no host synchronisation (PR #4069, Description: no
  * host-side synchronization in the steady-state forward). */
 moe_status_t moe_layer_forward(moe_layer_t* layer, void* stream);

@@ -91,6 +91,19 @@ moe::CompactArgs compact_args(moe_layer* l, int32_t T) {
   return ca;
 }
 
+// Operands of the last-arriver combine fused into FC2 (MOE_FLAG_FUSED_COMBINE),
+// or none.
+moe::FusedCombineArgs fused_combine_args(moe_layer* l) {
+  moe::FusedCombineArgs f;
+  memset(&f, 0, sizeof(f));
+  if (!(l->cfg.flags & MOE_FLAG_FUSED_COMBINE)) return f;
+  f.out = static_cast<uint16_t*>(l->out);
+  f.route_pos = region<int32_t>(l, MOE_REGION_ROUTE_POS);
+  f.route_w = region<float>(l, MOE_REGION_STAGED_W);
+  f.arrive = region<int32_t>(l, MOE_REGION_ARRIVE);
+  return f;
+}
+
 moe_status_t hip_fail(const char* what) {
   hipError_t e = hipGetLastError();
   return moe::fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -177,6 +190,10 @@ extern "C" moe_status_t moe_layer_create(const moe_config_t* cfg, int32_t expect
          moe::launch_tile_mx_scales(static_cast<const uint8_t*>(w->w2_scale),
                                     reinterpret_cast<uint32_t*>(l->ws + L.off[MOE_REGION_W2S]), E, H, I,
                                     (H + 255) / 256, I, false, stream) == 0;
+  // arrival counters of the fused combine start at zero (each forward leaves them so)
+  if (ok && (cfg->flags & MOE_FLAG_FUSED_COMBINE))
+    ok = moe::launch_fill_zero(reinterpret_cast<uint32_t*>(l->ws + L.off[MOE_REGION_ARRIVE]),
+                               (int64_t)(L.size[MOE_REGION_ARRIVE] / 4), stream) == 0;
   if (!ok) {
     delete l;
     return hip_fail("weight transform launch");
@@ -303,10 +320,11 @@ extern "C" moe_status_t moe_layer_forward(moe_layer_t* l, void* stream) {
     m2.y = region<uint16_t>(l, MOE_REGION_Y);
     m2.grid = l->grid_fc2;
     m2.w_e5m2 = m1.w_e5m2;
+    m2.fc = fused_combine_args(l);
     p = prof_begin(l, MOE_KERNEL_FC2, s);
     if (moe::launch_fc2_mx(m2, l->tac.block_m, stream) != 0) return hip_fail("fc2 launch");
     prof_end(l, p, s);
-    return combine(l, T, s, stream);
+    return m2.fc.out ? MOE_OK : combine(l, T, s, stream);
   }
 
   moe::GemmArgs g1;
@@ -355,11 +373,12 @@ extern "C" moe_status_t moe_layer_forward(moe_layer_t* l, void* stream) {
   g2.hdr = ca.hdr;
   g2.y = region<uint16_t>(l, MOE_REGION_Y);
   g2.grid = l->grid_fc2;
+  g2.fc = fused_combine_args(l);
   p = prof_begin(l, MOE_KERNEL_FC2, s);
   if (moe::launch_fc2(g2, l->tac.block_m, stream) != 0) return hip_fail("fc2 launch");
   prof_end(l, p, s);
 
-  return combine(l, T, s, stream);
+  return g2.fc.out ? MOE_OK : combine(l, T, s, stream);
 }
 
 extern "C" moe_status_t moe_read_status(moe_layer_t* l, void* stream, uint32_t* bits) {
@@ -377,7 +396,7 @@ extern "C" moe_status_t moe_read_status(moe_layer_t* l, void* stream, uint32_t* 
 extern "C" moe_status_t moe_layer_region(moe_layer_t* l, int32_t r, void** dptr, size_t* bytes) {
   moe::clear_error();
   if (!l || !dptr || !bytes) return moe::fail(MOE_ERR_INVALID_ARG, "NULL argument");
-  if (r < 0 || r > MOE_REGION_GATEUP) return moe::fail(MOE_ERR_INVALID_ARG, "unknown region %d", r);
+  if (r < 0 || r > MOE_REGION_ARRIVE) return moe::fail(MOE_ERR_INVALID_ARG, "unknown region %d", r);
   *dptr = l->ws + l->L.off[r];
   *bytes = l->L.size[r];
   return MOE_OK;

@@ -40,6 +40,7 @@
 
 #include <type_traits>
 
+#include "moe_combine_dev.h"
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -179,6 +180,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) float fsc[BT][2];             // final scale products
   __shared__ __attribute__((aligned(16))) uint32_t l2sink[kThreads];    // L2 prefetch landing words (never read)
   __shared__ __attribute__((aligned(16))) float red_s[FC1 ? C::WN * BT : 4];  // FC1 epilogue: partial amax
+  __shared__ int32_t cb_list[FC1 ? 1 : BT];  // FC2 fused combine: tokens this tile completes
+  __shared__ int32_t cb_count;
   auto ring = [&](auto stage) -> lds_u8* {
     constexpr int S = decltype(stage)::value;
     if constexpr (S == 0) return (lds_u8*)ring0;
@@ -312,6 +315,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
   if (v < v_end) {
     setup(v);
     prologue();
+  }
+  if constexpr (!FC1) {
+    if (a.fc.out) zero_unrouted_rows(a.fc, (int)a.hdr[kHdrTokens], a.top_k, a.n_rows);
   }
   for (; v < v_end; v += per_xcd) {
     float pf = 1.0f;
@@ -499,10 +505,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
             u32x2 o;
             o[0] = f32_to_bf16_rne(acc[nb][tb][0]) | (f32_to_bf16_rne(acc[nb][tb][1]) << 16);
             o[1] = f32_to_bf16_rne(acc[nb][tb][2]) | (f32_to_bf16_rne(acc[nb][tb][3]) << 16);
-            *reinterpret_cast<u32x2*>(a.y + (int64_t)(ep_p0 + t) * a.n_rows + n0 + n) = o;
+            uint16_t* dst = a.y + (int64_t)(ep_p0 + t) * a.n_rows + n0 + n;
+            if (a.fc.out)
+              store_y_coherent(dst, o[0], o[1]);  // read by the workgroup that completes the token
+            else
+              *reinterpret_cast<u32x2*>(dst) = o;
           }
         }
       }
+      if (a.fc.out)
+        arrive_and_combine<kThreads>(a.fc, a.y, a.sorted_route, a.top_k, a.n_rows, a.n_tiles, ep_p0, ep_rows, ep_nt,
+                                     (__attribute__((address_space(3))) int32_t*)cb_list,
+                                     (__attribute__((address_space(3))) int32_t*)&cb_count);
     }
   }
 }

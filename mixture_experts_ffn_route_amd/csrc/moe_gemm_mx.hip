@@ -26,6 +26,7 @@
 
 #include <type_traits>
 
+#include "moe_combine_dev.h"
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -123,6 +124,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring1[C::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t ring2[C::STAGES > 2 ? C::STAGE : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t ring3[C::STAGES > 3 ? C::STAGE : 16];
+  __shared__ int32_t cb_list[FC1 ? 1 : BT];  // FC2 fused combine: tokens this tile completes
+  __shared__ int32_t cb_count;
   auto ring = [&](auto stage) -> lds_u8* {
     constexpr int S = decltype(stage)::value;
     if constexpr (S == 0) return (lds_u8*)ring0;
@@ -151,6 +154,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
   const int sa_grp = (wn * C::NBH) / 4;
   const int sa_shift = 8 * ((wn * C::NBH) % 4);
 
+  if constexpr (!FC1) {
+    if (a.fc.out) zero_unrouted_rows(a.fc, (int)a.hdr[kHdrTokens], a.top_k, a.n_rows);
+  }
   for (int64_t v = v_begin + slot; v < v_end; v += per_xcd) {
     const int64_t group = v / ((int64_t)kGroupM * a.n_tiles);
     const int64_t rem = v - group * kGroupM * a.n_tiles;
@@ -344,10 +350,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
             u32x2 o;
             o[0] = f32_to_bf16_rne(acc[nb][tb][0]) | (f32_to_bf16_rne(acc[nb][tb][1]) << 16);
             o[1] = f32_to_bf16_rne(acc[nb][tb][2]) | (f32_to_bf16_rne(acc[nb][tb][3]) << 16);
-            *reinterpret_cast<u32x2*>(a.y + (int64_t)(p0 + t) * a.n_rows + n0 + n) = o;
+            uint16_t* dst = a.y + (int64_t)(p0 + t) * a.n_rows + n0 + n;
+            if (a.fc.out)
+              store_y_coherent(dst, o[0], o[1]);  // read by the workgroup that completes the token
+            else
+              *reinterpret_cast<u32x2*>(dst) = o;
           }
         }
       }
+      if (a.fc.out)
+        arrive_and_combine<kThreads>(a.fc, a.y, a.sorted_route, a.top_k, a.n_rows, a.n_tiles, p0, rows_valid, nt,
+                                     (__attribute__((address_space(3))) int32_t*)cb_list,
+                                     (__attribute__((address_space(3))) int32_t*)&cb_count);
     }
     __syncthreads();  // the next tile's DMA reuses the LDS the epilogue read
   }

@@ -51,7 +51,8 @@ moe_status_t validate_config(const moe_config_t* cfg, int32_t expected_m, int32_
     return fail(MOE_ERR_UNSUPPORTED, "top_k %d not in {1, 2, 4, 6, 8}", cfg->top_k);
   if (cfg->top_k > cfg->num_experts)
     return fail(MOE_ERR_INVALID_ARG, "top_k %d exceeds num_experts %d", cfg->top_k, cfg->num_experts);
-  if (cfg->flags & ~(uint32_t)(MOE_FLAG_CHECK_ROUTES | MOE_FLAG_PER_ROUTE_STAGING | MOE_FLAG_UNFUSED_FC1))
+  if (cfg->flags & ~(uint32_t)(MOE_FLAG_CHECK_ROUTES | MOE_FLAG_PER_ROUTE_STAGING | MOE_FLAG_UNFUSED_FC1 |
+                               MOE_FLAG_FUSED_COMBINE))
     return fail(MOE_ERR_INVALID_ARG, "unknown flag bits 0x%x", cfg->flags);
   if (cfg->weight_format == MOE_WEIGHT_E4M3_BLOCK128) {
     if (cfg->act_format != MOE_ACT_E4M3_1X128)
@@ -125,6 +126,7 @@ Layout compute_layout(const moe_config_t& cfg, const Tactic& t, int32_t max_rows
   L.size[MOE_REGION_W13S] = mx ? L.size[MOE_REGION_W13T] / 32 : 0;
   L.size[MOE_REGION_W2S] = mx ? L.size[MOE_REGION_W2T] / 32 : 0;
   L.size[MOE_REGION_GATEUP] = (cfg.flags & MOE_FLAG_UNFUSED_FC1) ? L.row_cap * 2 * I * 4 : 0;
+  L.size[MOE_REGION_ARRIVE] = (cfg.flags & MOE_FLAG_FUSED_COMBINE) ? (int64_t)max_rows * ((H + 255) / 256) * 4 : 0;
   L.size[kRegionBlkBase] = L.compact_blocks * E * 4;
   size_t off = 0;
   for (int r = 0; r < kNumRegions; ++r) {

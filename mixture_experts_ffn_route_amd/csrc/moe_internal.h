@@ -12,8 +12,8 @@ namespace moe {
 constexpr int kMaxExperts = 1024;
 constexpr int kCompactChunk = 4096;  // routes per compaction workgroup (256 lanes x 16)
 constexpr int kFuseRoutes = 2048;    // staging and compaction share one launch up to this many routes
-constexpr int kNumRegions = 19;
-constexpr int kRegionBlkBase = 18;   // internal: per-(compaction block, expert) bases
+constexpr int kNumRegions = 20;
+constexpr int kRegionBlkBase = 19;   // internal: per-(compaction block, expert) bases
 
 // Words of the device header (MOE_REGION_STATUS).
 enum HeaderWord : int {
@@ -91,6 +91,14 @@ int launch_compact(const CompactArgs& a, void* stream);
 // Stage and compact in one launch (routes <= kCompactChunk).
 int launch_stage_compact(const StageArgs& a, const CompactArgs& c, void* stream);
 
+// Operands of the last-arriver combine fused into FC2 (moe_combine_dev.h).
+struct FusedCombineArgs {
+  uint16_t* out;             // bf16 [T, H]; null: FC2 stores y only
+  const int32_t* route_pos;  // [T*K]
+  const float* route_w;      // [T*K] staged weights
+  int32_t* arrive;           // [max_rows, ceil(H/256)] arrival counters, zero between forwards
+};
+
 struct GemmArgs {
   // A operand: activation rows
   const uint8_t* a;        // e4m3 rows
@@ -114,6 +122,7 @@ struct GemmArgs {
   uint16_t* y;             // FC2: bf16 [R, H]
   float* gateup;           // FC1, unfused: FP32 gate/up rows [R, 2I] instead of the fused epilogue
   int32_t grid;
+  FusedCombineArgs fc;     // FC2: last-arriver combine into the output (fc.out null: none)
 };
 int launch_fc1(const GemmArgs& a, int block_m, void* stream);
 // Unfused FC1 second half: SwiGLU + 1x128 requant of the FP32 gate/up rows.
@@ -143,6 +152,7 @@ struct MxGemmArgs {
   uint16_t* y;               // FC2: bf16 [R, H]
   int32_t grid;
   int32_t w_e5m2;            // weight element type: 0 e4m3, 1 e5m2
+  FusedCombineArgs fc;       // FC2: last-arriver combine into the output (fc.out null: none)
 };
 int launch_fc1_mx(const MxGemmArgs& a, int block_m, void* stream);
 int launch_fc2_mx(const MxGemmArgs& a, int block_m, void* stream);
@@ -156,6 +166,8 @@ struct CombineArgs {
   uint16_t* out;
 };
 int launch_combine(const CombineArgs& a, void* stream);
+// Zero-fill of 32-bit words (the arrival counters at create).
+int launch_fill_zero(uint32_t* p, int64_t words, void* stream);
 
 // MXFP8 weight formats (either element type, E8M0 scales per 32).
 inline bool is_mx(int weight_format) {

@@ -161,3 +161,19 @@ def test_unfused_fc1_flag():
         L.moe_workspace_query(_cfg(weight_format=L.MOE_WEIGHT_MXFP8_E4M3, act_format=L.MOE_ACT_BF16,
                                    flags=L.MOE_FLAG_UNFUSED_FC1), 128, 4096, 1.0)
     assert ei.value.status == L.MOE_ERR_UNSUPPORTED
+
+
+def test_fused_combine_flag():
+    """MOE_FLAG_FUSED_COMBINE adds the int32 [max_rows, ceil(H/256)] arrival
+    counters and is accepted with either weight format."""
+    base = L.moe_workspace_query(_cfg(), 128, 4096, 1.0)
+    fus = L.moe_workspace_query(_cfg(flags=L.MOE_FLAG_CHECK_ROUTES | L.MOE_FLAG_FUSED_COMBINE), 128, 4096, 1.0)
+    assert fus - base == 4096 * 28 * 4
+    mx = _cfg(weight_format=L.MOE_WEIGHT_MXFP8_E4M3, act_format=L.MOE_ACT_BF16)
+    mx_base = L.moe_workspace_query(mx, 128, 4096, 1.0)
+    mx_fus = L.moe_workspace_query(_cfg(weight_format=L.MOE_WEIGHT_MXFP8_E4M3, act_format=L.MOE_ACT_BF16,
+                                        flags=L.MOE_FLAG_FUSED_COMBINE), 128, 4096, 1.0)
+    assert mx_fus - mx_base == 4096 * 28 * 4
+    with pytest.raises(L.MoEError) as ei:
+        L.moe_workspace_query(_cfg(flags=16), 128, 4096, 1.0)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARG
