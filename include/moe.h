@@ -250,12 +250,16 @@ moe_status_t moe_layer_region(moe_layer_t* layer, int32_t region, void** dptr, s
 /* The tactic chosen at create time. tactic: [host out]. */
 moe_status_t moe_layer_tactic(const moe_layer_t* layer, moe_tactic_t* tactic);
 
-/* Optional per-kernel timing with HIP events recorded around each launch on
- * the launch stream.  enable != 0 starts (and resets) accumulation.
- * moe_profile_read synchronises, then returns, per MOE_KERNEL_* class, the
- * summed milliseconds and the number of launches timed (host arrays of
- * MOE_KERNEL_COUNT). */
-moe_status_t moe_profile_enable(moe_layer_t* layer, int32_t enable);
+/* Optional per-kernel timing with HIP events recorded around the launches
+ * of the selected kernel classes on the launch stream.  kernel_mask: bit
+ * (1 << MOE_KERNEL_*) per class to time, MOE_PROFILE_ALL for all of them,
+ * 0 to stop; a non-zero mask starts (and resets) accumulation.  Each event
+ * pair costs a few microseconds of stream time, so time only the classes
+ * needed.  moe_profile_read synchronises, then returns, per MOE_KERNEL_*
+ * class, the summed milliseconds and the number of launches timed (host
+ * arrays of MOE_KERNEL_COUNT). */
+#define MOE_PROFILE_ALL ((1u << MOE_KERNEL_COUNT) - 1u)
+moe_status_t moe_profile_enable(moe_layer_t* layer, uint32_t kernel_mask);
 moe_status_t moe_profile_read(moe_layer_t* layer, double* ms_total, int64_t* launches);
 
 /* Release the handle (host memory only; the workspace stays the caller's).

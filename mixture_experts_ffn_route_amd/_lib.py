@@ -44,6 +44,7 @@ REGIONS = {
     "w13s": 15, "w2s": 16, "gateup": 17, "arrive": 18,
 }
 KERNELS = ("stage", "compact", "fc1", "fc2", "combine")
+PROFILE_ALL = (1 << len(KERNELS)) - 1
 
 # Every symbol include/moe.h declares.
 EXPORTS = (
@@ -97,7 +98,7 @@ def _load() -> ctypes.CDLL:
         "moe_read_status": (i32, [vp, vp, POINTER(c_uint32)]),
         "moe_layer_region": (i32, [vp, i32, POINTER(vp), POINTER(c_size_t)]),
         "moe_layer_tactic": (i32, [vp, POINTER(moe_tactic_t)]),
-        "moe_profile_enable": (i32, [vp, i32]),
+        "moe_profile_enable": (i32, [vp, c_uint32]),
         "moe_profile_read": (i32, [vp, POINTER(c_double), POINTER(c_int64)]),
         "moe_layer_destroy": (i32, [vp]),
         "moe_token_bucket": (i32, [i32]),
@@ -180,8 +181,9 @@ def moe_layer_tactic(layer: int) -> dict:
     return {name: getattr(t, name) for name, _ in t._fields_}
 
 
-def moe_profile_enable(layer: int, enable: bool) -> None:
-    _check(_lib.moe_profile_enable(layer, 1 if enable else 0))
+def moe_profile_enable(layer: int, kernel_mask: int) -> None:
+    """kernel_mask: bit (1 << k) per KERNELS[k] class to time, PROFILE_ALL, or 0."""
+    _check(_lib.moe_profile_enable(layer, kernel_mask))
 
 
 def moe_profile_read(layer: int) -> dict:

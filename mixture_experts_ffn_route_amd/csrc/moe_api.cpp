@@ -31,8 +31,8 @@ struct moe_layer {
   bool compacted;  // the staging launch also compacted the routes (small batches)
   void* out;
   int32_t grid_fc1, grid_fc2;
-  // profiling
-  bool prof;
+  // profiling: event pairs around the launches of the classes in prof_mask
+  uint32_t prof_mask;
   std::vector<EventPair> pending;
   std::vector<hipEvent_t> pool;
   double ms[MOE_KERNEL_COUNT];
@@ -59,7 +59,7 @@ hipEvent_t take_event(moe_layer* l) {
 
 // Records a start event if profiling; returns the pending index or -1.
 int prof_begin(moe_layer* l, int kind, hipStream_t s) {
-  if (!l->prof) return -1;
+  if (!(l->prof_mask & (1u << kind))) return -1;
   EventPair p{take_event(l), take_event(l), kind};
   if (!p.start || !p.stop) return -1;
   (void)hipEventRecord(p.start, s);
@@ -198,7 +198,7 @@ extern "C" moe_status_t moe_layer_create(const moe_config_t* cfg, int32_t expect
     delete l;
     return hip_fail("weight transform launch");
   }
-  l->prof = false;
+  l->prof_mask = 0;
   memset(l->ms, 0, sizeof(l->ms));
   memset(l->launches, 0, sizeof(l->launches));
   *out = l;
@@ -416,10 +416,11 @@ extern "C" moe_status_t moe_layer_tactic(const moe_layer_t* l, moe_tactic_t* t) 
   return MOE_OK;
 }
 
-extern "C" moe_status_t moe_profile_enable(moe_layer_t* l, int32_t enable) {
+extern "C" moe_status_t moe_profile_enable(moe_layer_t* l, uint32_t kernel_mask) {
   moe::clear_error();
   if (!l) return moe::fail(MOE_ERR_INVALID_ARG, "layer is NULL");
-  l->prof = enable != 0;
+  if (kernel_mask & ~MOE_PROFILE_ALL) return moe::fail(MOE_ERR_INVALID_ARG, "unknown kernel classes 0x%x", kernel_mask);
+  l->prof_mask = kernel_mask;
   memset(l->ms, 0, sizeof(l->ms));
   memset(l->launches, 0, sizeof(l->launches));
   return MOE_OK;

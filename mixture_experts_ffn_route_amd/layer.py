@@ -76,8 +76,13 @@ class MoELayer:
     def tactic(self) -> dict:
         return L.moe_layer_tactic(self.handle)
 
-    def profile(self, enable: bool) -> None:
-        L.moe_profile_enable(self.handle, enable)
+    def profile(self, enable=True, kernels=None) -> None:
+        """Time every kernel class (``enable`` true), the named ``kernels``
+        only (e.g. ``("fc1",)``), or stop (``enable`` false)."""
+        mask = 0
+        if enable:
+            mask = L.PROFILE_ALL if kernels is None else sum(1 << L.KERNELS.index(k) for k in kernels)
+        L.moe_profile_enable(self.handle, mask)
 
     def profile_read(self) -> dict:
         return L.moe_profile_read(self.handle)

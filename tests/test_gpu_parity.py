@@ -304,3 +304,24 @@ def test_unfused_fc1_equals_fused(cfg, expected_m):
         # mistakes give O(1) errors
         err = np.abs(gu[lo:hi] - want)
         assert np.all(err <= 1e-4 * np.abs(want).max(axis=1, keepdims=True) + 1e-30), f"expert {e}: {err.max():.3e}"
+
+
+def test_profile_mask_times_selected_kernels():
+    """Events are recorded only around the selected kernel classes."""
+    shape = CONFIGS["tiny"]
+    inp = make_layer_inputs(shape, seed=12)
+    dev = to_device(inp)
+    layer = make_layer(shape, dev)
+    layer.profile(True, kernels=("fc1",))
+    for _ in range(3):
+        run_forward(layer, dev)
+    prof = layer.profile_read()
+    assert prof["fc1"][1] == 3 and prof["fc1"][0] > 0
+    assert all(n == 0 for k, (ms, n) in prof.items() if k != "fc1")
+    layer.profile(True)
+    run_forward(layer, dev)
+    prof = layer.profile_read()
+    assert prof["stage"][1] == 1 and prof["fc2"][1] == 1 and prof["combine"][1] == 1
+    layer.profile(False)
+    with pytest.raises(L.MoEError):
+        L.moe_profile_enable(layer.handle, 1 << 7)
