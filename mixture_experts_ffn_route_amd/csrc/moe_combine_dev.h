@@ -47,42 +47,57 @@ __device__ __forceinline__ cb_u32x4 load_y16(const uint16_t* p) {
   }
 }
 
-// Columns [c, c + 8) of token t.  Slots that are not kept contribute
-// fmaf(0, 0, acc), exactly as the standalone kernel always has.
-template <bool kCoherent>
-__device__ __forceinline__ void combine8(const uint16_t* y, const int32_t* route_pos, const float* route_w,
-                                         int64_t t, int K, int hidden, int c, uint16_t* out) {
-  float w[8];
-  cb_u32x4 raw[8];
+// Columns [c, c + 8) of token t, for K routes per token.  Slots that are
+// not kept contribute fmaf(0, 0, acc), exactly as the standalone kernel
+// always has.  Every slot's position is loaded first, then every slot's row
+// without a branch (a slot that is not kept reads row 0, which exists, and
+// then counts as zero), so the loads take two round trips in all.
+template <int K, bool kCoherent>
+__device__ __forceinline__ void combine8_k(const uint16_t* y, const int32_t* route_pos, const float* route_w,
+                                           int64_t t, int hidden, int c, uint16_t* out) {
+  int pos[K];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    w[k] = 0.f;
-    raw[k] = cb_u32x4{0u, 0u, 0u, 0u};
-    if (k < K) {
-      const int p = route_pos[t * K + k];
-      if (p >= 0) {
-        w[k] = route_w[t * K + k];
-        raw[k] = load_y16<kCoherent>(y + (int64_t)p * hidden + c);
-      }
+  for (int k = 0; k < K; ++k) pos[k] = route_pos[t * K + k];
+  float w[K];
+  cb_u32x4 raw[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const bool keep = pos[k] >= 0;
+    w[k] = route_w[t * K + k];
+    raw[k] = load_y16<kCoherent>(y + (int64_t)(keep ? pos[k] : 0) * hidden + c);
+    if (!keep) {
+      w[k] = 0.f;
+      raw[k] = cb_u32x4{0u, 0u, 0u, 0u};
     }
   }
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    if (k < K) {
+  for (int k = 0; k < K; ++k) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = fmaf(w[k], bf16_to_f32(raw[k][i] & 0xffffu), acc[2 * i]);
-        acc[2 * i + 1] = fmaf(w[k], bf16_to_f32(raw[k][i] >> 16), acc[2 * i + 1]);
-      }
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] = fmaf(w[k], bf16_to_f32(raw[k][i] & 0xffffu), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(w[k], bf16_to_f32(raw[k][i] >> 16), acc[2 * i + 1]);
     }
   }
   cb_u32x4 o;
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16_rne(acc[2 * i]) | (f32_to_bf16_rne(acc[2 * i + 1]) << 16);
   *reinterpret_cast<cb_u32x4*>(out + t * hidden + c) = o;
+}
+
+// K in {1, 2, 4, 6, 8} (the layer configuration is validated to those).
+template <bool kCoherent>
+__device__ __forceinline__ void combine8(const uint16_t* y, const int32_t* route_pos, const float* route_w,
+                                         int64_t t, int K, int hidden, int c, uint16_t* out) {
+  switch (K) {
+    case 1: combine8_k<1, kCoherent>(y, route_pos, route_w, t, hidden, c, out); break;
+    case 2: combine8_k<2, kCoherent>(y, route_pos, route_w, t, hidden, c, out); break;
+    case 4: combine8_k<4, kCoherent>(y, route_pos, route_w, t, hidden, c, out); break;
+    case 6: combine8_k<6, kCoherent>(y, route_pos, route_w, t, hidden, c, out); break;
+    default: combine8_k<8, kCoherent>(y, route_pos, route_w, t, hidden, c, out); break;
+  }
 }
 
 // Kept routes of token t (K <= 8).  The loads are unconditional (slot index

@@ -31,18 +31,46 @@ __device__ __forceinline__ uint64_t peers_of(int e, bool valid, int nbits) {
   return m;
 }
 
+// The routes a wave walks in block blk: the block's routes split into
+// kCompactWaves ascending contiguous ranges of whole 64-route items (at most
+// kItems each), so a small batch spreads over every wave.  Sweep and scatter
+// use the same split.
+struct WaveRange {
+  int64_t base;
+  int items;
+};
+__device__ inline WaveRange wave_range(const CompactArgs& a, int blk, int wave) {
+  const int64_t b0 = (int64_t)blk * kCompactChunk;
+  const int64_t n = min((int64_t)a.routes - b0, (int64_t)kCompactChunk);
+  const int items = (int)((n + 64 * kCompactWaves - 1) / (64 * kCompactWaves));
+  return WaveRange{b0 + (int64_t)wave * items * 64, items};
+}
+
 // Walk this block's routes wave by wave.  hist[w*E + e] holds wave w's
 // running count; rank[i] receives the count of same-expert routes before
-// item i within this wave's range.
-__device__ inline void sweep(const CompactArgs& a, int blk, int* hist, int* rank, int* expert) {
+// item i within this wave's range.  ids_lds: the staged expert ids in LDS
+// (the fused staging kernel keeps them there), else they are read from
+// a.staged_idx.
+__device__ inline void sweep(const CompactArgs& a, int blk, int* hist, int* rank, int* expert,
+                             const int* ids_lds = nullptr) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nbits = id_bits(a.num_experts);
-  const int64_t base = (int64_t)blk * kCompactChunk + (int64_t)wave * (kCompactChunk / kCompactWaves);
+  const WaveRange wr = wave_range(a, blk, wave);
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // All of this lane's expert ids first: the histogram updates below go
+  // through a generic pointer, so a load placed after one of them would
+  // wait for the previous item's load to return.
+  int ids[kItems];
 #pragma unroll
   for (int it = 0; it < kItems; ++it) {
-    const int64_t r = base + it * 64 + lane;
-    const int e = r < a.routes ? a.staged_idx[r] : -1;
+    const int64_t r = wr.base + it * 64 + lane;
+    ids[it] = -1;
+    if (it < wr.items && r < a.routes) ids[it] = ids_lds ? ids_lds[r] : a.staged_idx[r];
+  }
+#pragma unroll
+  for (int it = 0; it < kItems; ++it) {
+    if (it >= wr.items) break;
+    const int e = ids[it];
     const bool valid = e >= 0;
     const uint64_t pm = peers_of(e, valid, nbits);
     const int below = __popcll(pm & lt);
@@ -144,10 +172,11 @@ __device__ inline void scatter(const CompactArgs& a, int blk, int* hist, const i
   }
   __syncthreads();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t base = (int64_t)blk * kCompactChunk + (int64_t)wave * (kCompactChunk / kCompactWaves);
+  const WaveRange wr = wave_range(a, blk, wave);
 #pragma unroll
   for (int it = 0; it < kItems; ++it) {
-    const int64_t r = base + it * 64 + lane;
+    if (it >= wr.items) break;
+    const int64_t r = wr.base + it * 64 + lane;
     if (r >= a.routes) continue;
     const int e = expert[it];
     int p = -1;
@@ -164,8 +193,8 @@ __device__ inline void scatter(const CompactArgs& a, int blk, int* hist, const i
 }
 
 // Single-workgroup compaction (routes <= kCompactChunk): count, scan,
-// scatter.  `lds` holds (kCompactWaves + 2) * E + 3 ints.
-__device__ inline void compact_one_workgroup(const CompactArgs& a, int* lds) {
+// scatter.  `lds` holds (kCompactWaves + 2) * E + 3 ints; ids_lds as in sweep.
+__device__ inline void compact_one_workgroup(const CompactArgs& a, int* lds, const int* ids_lds = nullptr) {
   const int E = a.num_experts;
   int* hist = lds;                        // [waves, E]
   int* cnt = hist + kCompactWaves * E;    // [E]
@@ -174,7 +203,7 @@ __device__ inline void compact_one_workgroup(const CompactArgs& a, int* lds) {
   int rank[kItems], expert[kItems];
   clear_hist(hist, kCompactWaves * E);
   __syncthreads();
-  sweep(a, 0, hist, rank, expert);
+  sweep(a, 0, hist, rank, expert, ids_lds);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kCompactThreads) {
     int s = 0;
@@ -187,7 +216,7 @@ __device__ inline void compact_one_workgroup(const CompactArgs& a, int* lds) {
   scatter(a, 0, hist, tmp, rank, expert);  // tmp holds the full exclusive offsets
 }
 
-inline size_t compact_one_workgroup_lds(int num_experts) {
+__host__ __device__ inline size_t compact_one_workgroup_lds(int num_experts) {
   return (size_t)(kCompactWaves * num_experts + num_experts + num_experts + 1 + 2) * 4;
 }
 

@@ -99,8 +99,10 @@ __device__ inline void split_mx(const StageArgs& a, int64_t g, int64_t groups) {
 }
 
 // One thread per token slot row in [0, max_rows).  Live rows are checked and
-// masked; rows past the live count are staged as masked.
-__device__ inline void stage_route_row(const StageArgs& a, int t) {
+// masked; rows past the live count are staged as masked.  ids_lds (live rows
+// only): a copy of the staged expert ids for the compaction of the same
+// workgroup.
+__device__ inline void stage_route_row(const StageArgs& a, int t, int* ids_lds = nullptr) {
   const int K = a.top_k;
   uint32_t bits = 0;
   int ids[8];
@@ -158,6 +160,7 @@ __device__ inline void stage_route_row(const StageArgs& a, int t) {
     if (k < K) {
       a.staged_idx[(int64_t)t * K + k] = act[k] ? ids[k] : -1;
       a.staged_w[(int64_t)t * K + k] = act[k] ? ws[k] : 0.0f;
+      if (ids_lds && t < a.tokens) ids_lds[t * K + k] = act[k] ? ids[k] : -1;
     }
   }
   if (bits) atomicOr(a.hdr + kHdrStatus, bits);
@@ -183,7 +186,7 @@ __global__ __launch_bounds__(256) void stage_routes_kernel(StageArgs a) {
   if (t < a.max_rows) stage_route_row(a, t);
 }
 
-// Small batches (routes <= kCompactChunk): one launch stages everything.
+// Small batches (routes <= kFuseRoutes): one launch stages everything.
 // Blocks [0, quant_blocks) quantise (or split) x; the last block resets the
 // header, stages and checks every route row, then compacts the routes as a
 // single workgroup, so the forward starts at FC1.
@@ -198,11 +201,13 @@ __global__ __launch_bounds__(256) void stage_fused_kernel(StageArgs a, CompactAr
       quant_1x128(a, g, groups, copies);
     return;
   }
+  // the staged ids of the live rows stay in LDS for the compaction
+  int* ids_lds = lds + compact_one_workgroup_lds(c.num_experts) / 4;
   reset_header(a);
   __syncthreads();
-  for (int t = threadIdx.x; t < a.max_rows; t += 256) stage_route_row(a, t);
-  __syncthreads();  // this workgroup's route stores are visible to its own loads
-  compact_one_workgroup(c, lds);
+  for (int t = threadIdx.x; t < a.max_rows; t += 256) stage_route_row(a, t, ids_lds);
+  __syncthreads();
+  compact_one_workgroup(c, lds, ids_lds);
 }
 
 static void quant_grid(const StageArgs& a, int64_t* groups, int* blocks, int* copies) {
@@ -231,8 +236,8 @@ int launch_stage_compact(const StageArgs& a, const CompactArgs& c, void* stream)
   int64_t groups;
   int qblocks, copies;
   quant_grid(a, &groups, &qblocks, &copies);
-  hipLaunchKernelGGL(stage_fused_kernel, dim3(qblocks + 1), dim3(256), compact_one_workgroup_lds(c.num_experts), s, a,
-                     c, groups, copies, qblocks);
+  const size_t lds = compact_one_workgroup_lds(c.num_experts) + (size_t)c.routes * 4;
+  hipLaunchKernelGGL(stage_fused_kernel, dim3(qblocks + 1), dim3(256), lds, s, a, c, groups, copies, qblocks);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
