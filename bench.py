@@ -133,6 +133,8 @@ def main():
     ap.add_argument("--weights", default="fp8_block", choices=["fp8_block", "mxfp8", "mxfp8_e5m2"],
                     help="fp8_block: e4m3 + 128x128 scales, e4m3 1x128 activations; "
                          "mxfp8 / mxfp8_e5m2: e4m3 / e5m2 + E8M0 per 32 weights x BF16 activations")
+    ap.add_argument("--ffn", default="two", choices=["two", "persistent"],
+                    help="two: FC1 and FC2 launches; persistent: one launch, FC2 tiles start as their rows are ready")
     ap.add_argument("--combine", default="separate", choices=["separate", "fused"],
                     help="separate: combine kernel after FC2; fused: last-arriver combine inside FC2")
     ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens for the CPU oracle baseline (0: skip)")
@@ -161,6 +163,9 @@ def main():
     peak = FP8_PEAK_TFLOPS / 2 if mx else FP8_PEAK_TFLOPS
     from mixture_experts_ffn_route_amd import _lib as L
     flags = L.MOE_FLAG_CHECK_ROUTES | (L.MOE_FLAG_FUSED_COMBINE if args.combine == "fused" else 0)
+    persistent = args.ffn == "persistent"
+    if persistent:
+        flags |= L.MOE_FLAG_PERSISTENT_FFN
 
     def measure(tokens, steps, warmup, time_fc1=True):
         shape = MoEShape(tokens, base.hidden, base.intermediate, base.experts, base.top_k, base.routing)
@@ -209,7 +214,7 @@ def main():
         B = workload_bytes(shape, counts, T, mx=mx)
         kern = {k: v[0] / max(v[1], 1) for k, v in prof.items() if k != "fc1_timed"}
         rec = {"tokens": T, "ms_per_step": sec * 1e3, "tflops": flops / sec / 1e12, "gbs": B / sec / 1e9,
-               "pct_mfma_peak": 100 * flops / sec / 1e12 / peak, "weights": args.weights, "combine": args.combine,
+               "pct_mfma_peak": 100 * flops / sec / 1e12 / peak, "weights": args.weights, "combine": args.combine, "ffn": args.ffn,
                "pct_hbm_peak": 100 * B / sec / 1e9 / HBM_PEAK_GBS,
                "kernel_ms": kern, "tactic": layer.tactic(), "status": status}
         log("[sweep]", json.dumps(rec))
@@ -238,7 +243,8 @@ def main():
     B = workload_bytes(shape, counts, T, mx=mx)
     fc1_ms, fc1_n = prof["fc1_timed"]
     fc1_avg_s = fc1_ms / max(fc1_n, 1) / 1e3
-    achieved = fc1_flops(R, H, I) / fc1_avg_s / 1e12
+    # with the persistent launch the "fc1" class times FC1 and FC2 together
+    achieved = (flops if persistent else fc1_flops(R, H, I)) / fc1_avg_s / 1e12
     kern = {k: round(v[0] / max(v[1], 1), 4) for k, v in prof.items() if k != "fc1_timed"}
     log(f"[bench] T={T} R={R} status={status} ms/step={sec * 1e3:.3f} kernel avg ms={kern} tactic={layer.tactic()}")
     log(f"[bench] step {flops / sec / 1e12:.1f} TFLOP/s, {B / sec / 1e9:.0f} GB/s algorithmic")
@@ -264,12 +270,13 @@ def main():
         "vs_baseline": None,
         "dtype": f"bf16 x mxfp8_{mx}" if mx else "fp8_e4m3",
         "data": "synthetic",
-        "config": {"workload": workload, "tokens": T, "routes": R, "combine": args.combine,
+        "config": {"workload": workload, "tokens": T, "routes": R, "combine": args.combine, "ffn": args.ffn,
                    "hbm_gbs_algorithmic": round(B / sec / 1e9, 1),
                    "pct_mfma_peak": round(100 * flops / sec / 1e12 / peak, 2),
                    "kernel_avg_ms": kern},
         "roofline": {"bound": "mfma",
                      "kernel": ("fc1 (MX-scaled FP8 grouped GEMM, two activation terms + SwiGLU + bf16 split)" if mx
+                                else "fc1+fc2 persistent (FP8 grouped GEMMs, one launch)" if persistent
                                 else "fc1 (FP8 grouped GEMM + SwiGLU + 1x128 requant)"),
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": stored_traffic(workload),

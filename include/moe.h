@@ -104,7 +104,16 @@ enum {
    * every forward.  The y rows are then stored write-through so that a tile
    * on another XCD can read them; on MI355X this costs more than the
    * separate combine launch it saves, so the flag is off by default. */
-  MOE_FLAG_FUSED_COMBINE = 8u
+  MOE_FLAG_FUSED_COMBINE = 8u,
+  /* Persistent FC1->FC2 (E4M3_BLOCK128 weights only): one cooperative launch
+   * runs every FC1 tile and then every FC2 tile of each workgroup, and an
+   * FC2 tile starts as soon as all FC1 column tiles of its row tile have
+   * stored their rows (per-row-tile readiness counters in MOE_REGION_READY),
+   * instead of after the whole FC1 launch (SM90 pull-style MegaMoE,
+   * flashinfer PR #4688: persistent kernel with fc1_done readiness flags).
+   * Same arithmetic, same bits.  The h rows are then stored write-through so
+   * that a tile on another XCD can read them. */
+  MOE_FLAG_PERSISTENT_FFN = 16u
 };
 
 /* Device status bits (moe_read_status). */
@@ -112,7 +121,9 @@ enum {
   MOE_DEV_BAD_EXPERT = 1u,   /* an expert id outside [-1, E) was masked */
   MOE_DEV_DUPLICATE = 2u,    /* a repeated expert within a token was masked (lowest slot kept) */
   MOE_DEV_NONFINITE = 4u,    /* an active route with a NaN/inf weight was masked */
-  MOE_DEV_CAPACITY = 8u      /* routes beyond the row capacity were dropped */
+  MOE_DEV_CAPACITY = 8u,     /* routes beyond the row capacity were dropped */
+  MOE_DEV_WAIT_TIMEOUT = 16u /* MOE_FLAG_PERSISTENT_FFN: an FC2 tile gave up waiting for its FC1 rows
+                                (never expected; the output is then not valid) */
 };
 
 typedef struct {
@@ -171,8 +182,10 @@ enum {
   MOE_REGION_W13S = 15,         /* MXFP8: w13 E8M0 tiled at create, 1 KB per w13 tile (empty for FP8) */
   MOE_REGION_W2S = 16,          /* MXFP8: w2 E8M0 tiled at create, 1 KB per w2 tile (empty for FP8) */
   MOE_REGION_GATEUP = 17,       /* MOE_FLAG_UNFUSED_FC1: float32 [row_cap, 2I] gate then up columns (else empty) */
-  MOE_REGION_ARRIVE = 18        /* MOE_FLAG_FUSED_COMBINE: int32 [max_rows, ceil(H/256)] arrival counters,
+  MOE_REGION_ARRIVE = 18,       /* MOE_FLAG_FUSED_COMBINE: int32 [max_rows, ceil(H/256)] arrival counters,
                                    zero between forwards (else empty) */
+  MOE_REGION_READY = 19         /* MOE_FLAG_PERSISTENT_FFN: int32 [max_m_tiles] finished FC1 column tiles
+                                   per row tile, zeroed by the compaction (else empty) */
 };
 
 /* Kernel classes timed by the optional profiler. */

@@ -33,15 +33,17 @@ MOE_FLAG_CHECK_ROUTES = 1
 MOE_FLAG_PER_ROUTE_STAGING = 2
 MOE_FLAG_UNFUSED_FC1 = 4
 MOE_FLAG_FUSED_COMBINE = 8
+MOE_FLAG_PERSISTENT_FFN = 16
 MOE_DEV_BAD_EXPERT = 1
 MOE_DEV_DUPLICATE = 2
 MOE_DEV_NONFINITE = 4
 MOE_DEV_CAPACITY = 8
+MOE_DEV_WAIT_TIMEOUT = 16
 
 REGIONS = {
     "status": 0, "staged_idx": 1, "staged_w": 2, "xq": 3, "xs": 4, "counts": 5, "offsets": 6,
     "sorted_route": 7, "route_pos": 8, "hq": 9, "hs": 10, "y": 11, "tiles": 12, "w13t": 13, "w2t": 14,
-    "w13s": 15, "w2s": 16, "gateup": 17, "arrive": 18,
+    "w13s": 15, "w2s": 16, "gateup": 17, "arrive": 18, "ready": 19,
 }
 KERNELS = ("stage", "compact", "fc1", "fc2", "combine")
 PROFILE_ALL = (1 << len(KERNELS)) - 1

@@ -31,6 +31,7 @@ struct moe_layer {
   bool compacted;  // the staging launch also compacted the routes (small batches)
   void* out;
   int32_t grid_fc1, grid_fc2;
+  int32_t grid_persist;  // MOE_FLAG_PERSISTENT_FFN: cooperative grid of the FC1->FC2 launch
   // profiling: event pairs around the launches of the classes in prof_mask
   uint32_t prof_mask;
   std::vector<EventPair> pending;
@@ -88,6 +89,7 @@ moe::CompactArgs compact_args(moe_layer* l, int32_t T) {
   ca.sorted_route = region<int32_t>(l, MOE_REGION_SORTED_ROUTE);
   ca.route_pos = region<int32_t>(l, MOE_REGION_ROUTE_POS);
   ca.tiles = region<int32_t>(l, MOE_REGION_TILES);
+  ca.ready = (l->cfg.flags & MOE_FLAG_PERSISTENT_FFN) ? region<int32_t>(l, MOE_REGION_READY) : nullptr;
   return ca;
 }
 
@@ -174,6 +176,12 @@ extern "C" moe_status_t moe_layer_create(const moe_config_t* cfg, int32_t expect
   };
   l->grid_fc1 = grid(1);
   l->grid_fc2 = grid(2);
+  l->grid_persist = 0;
+  if (cfg->flags & MOE_FLAG_PERSISTENT_FFN) {
+    // every workgroup must be resident at once (cooperative launch)
+    const int g = (cus * moe::gemm_persist_max_workgroups_per_cu(t.block_m) / 8) * 8;
+    l->grid_persist = g < 8 ? 8 : g;
+  }
   // weight codes -> kernel tile order, stream-ordered before any forward
   uint8_t* w13t = l->ws + L.off[MOE_REGION_W13T];
   uint8_t* w2t = l->ws + L.off[MOE_REGION_W2T];
@@ -348,12 +356,15 @@ extern "C" moe_status_t moe_layer_forward(moe_layer_t* l, void* stream) {
   g1.grid = l->grid_fc1;
   const bool unfused = (c.flags & MOE_FLAG_UNFUSED_FC1) != 0;
   g1.gateup = unfused ? region<float>(l, MOE_REGION_GATEUP) : nullptr;
-  p = prof_begin(l, MOE_KERNEL_FC1, s);
-  if (moe::launch_fc1(g1, l->tac.block_m, stream) != 0) return hip_fail("fc1 launch");
-  if (unfused && moe::launch_swiglu_quant(g1.gateup, (int32_t)l->L.row_cap, c.intermediate, g1.hdr, g1.hq, g1.hs,
-                                          stream) != 0)
-    return hip_fail("swiglu launch");
-  prof_end(l, p, s);
+  const bool persistent = (c.flags & MOE_FLAG_PERSISTENT_FFN) != 0;
+  if (!persistent) {
+    p = prof_begin(l, MOE_KERNEL_FC1, s);
+    if (moe::launch_fc1(g1, l->tac.block_m, stream) != 0) return hip_fail("fc1 launch");
+    if (unfused && moe::launch_swiglu_quant(g1.gateup, (int32_t)l->L.row_cap, c.intermediate, g1.hdr, g1.hq, g1.hs,
+                                            stream) != 0)
+      return hip_fail("swiglu launch");
+    prof_end(l, p, s);
+  }
 
   moe::GemmArgs g2;
   memset(&g2, 0, sizeof(g2));
@@ -374,6 +385,19 @@ extern "C" moe_status_t moe_layer_forward(moe_layer_t* l, void* stream) {
   g2.y = region<uint16_t>(l, MOE_REGION_Y);
   g2.grid = l->grid_fc2;
   g2.fc = fused_combine_args(l);
+  if (persistent) {
+    // FC1 and FC2 in one launch, timed as the FC1 class (FC2 has no launch)
+    moe::PersistArgs q;
+    q.ready = region<int32_t>(l, MOE_REGION_READY);
+    q.need = c.intermediate / 128;
+    q.status = region<uint32_t>(l, MOE_REGION_STATUS) + moe::kHdrStatus;
+    g1.grid = g2.grid = l->grid_persist;
+    p = prof_begin(l, MOE_KERNEL_FC1, s);
+    if (moe::launch_fc1_fc2(g1, g2, q, l->tac.block_m, l->grid_persist, stream) != 0)
+      return hip_fail("persistent fc1+fc2 launch");
+    prof_end(l, p, s);
+    return g2.fc.out ? MOE_OK : combine(l, T, s, stream);
+  }
   p = prof_begin(l, MOE_KERNEL_FC2, s);
   if (moe::launch_fc2(g2, l->tac.block_m, stream) != 0) return hip_fail("fc2 launch");
   prof_end(l, p, s);
@@ -396,7 +420,7 @@ extern "C" moe_status_t moe_read_status(moe_layer_t* l, void* stream, uint32_t* 
 extern "C" moe_status_t moe_layer_region(moe_layer_t* l, int32_t r, void** dptr, size_t* bytes) {
   moe::clear_error();
   if (!l || !dptr || !bytes) return moe::fail(MOE_ERR_INVALID_ARG, "NULL argument");
-  if (r < 0 || r > MOE_REGION_ARRIVE) return moe::fail(MOE_ERR_INVALID_ARG, "unknown region %d", r);
+  if (r < 0 || r > MOE_REGION_READY) return moe::fail(MOE_ERR_INVALID_ARG, "unknown region %d", r);
   *dptr = l->ws + l->L.off[r];
   *bytes = l->L.size[r];
   return MOE_OK;

@@ -152,6 +152,7 @@ __device__ inline void finish_counts(const CompactArgs& a, int* cnt, int* tmp, i
     for (int p = lo; p < kept_hi; p += a.block_m, ++m) {
       a.tiles[2 * m] = e;
       a.tiles[2 * m + 1] = p;
+      if (a.ready) a.ready[m] = 0;
     }
   }
   if (threadIdx.x == 0) a.hdr[kHdrMTiles] = (uint32_t)ntiles;

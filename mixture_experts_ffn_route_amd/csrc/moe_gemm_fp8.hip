@@ -130,6 +130,28 @@ __device__ __forceinline__ void dma4(const float* src, const lds_u8* lds_wave_ba
                :: "v"(src), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
 }
 
+// Scale loads of the persistent FC2 phase read rows that FC1 tiles on other
+// XCDs have just written, and two rows share a cache line, so they are made
+// at agent scope (sc1) instead of from a possibly stale L2 line.
+template <bool kCoherent>
+__device__ __forceinline__ void dma4_scale(const float* src, const lds_u8* lds_wave_base) {
+  if constexpr (kCoherent)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off sc1"
+                 :: "v"(src), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
+  else
+    dma4(src, lds_wave_base);
+}
+
+// Write-through store (agent scope) of h codes and scales in the persistent
+// launch, where FC2 tiles on other XCDs read them within the same kernel.
+__device__ __forceinline__ void store_wt_u32(uint8_t* p, uint32_t v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Polls of a readiness counter before a persistent FC2 tile gives up (each
+// poll sleeps ~0.25 us: ~0.25 s in all, far beyond any FC1 phase).
+constexpr int kSpinLimit = 1 << 20;
+
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -168,6 +190,8 @@ struct Cfg {
 template <int BT, bool FC1>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
   using C = Cfg<BT>;
+  constexpr bool PERSIST = false;
+  const PersistArgs q{};
   // One LDS object per ring stage: the compiler tracks LDS-DMA per object,
   // so reading one stage never waits for the DMA still filling another.
   __shared__ __attribute__((aligned(1024))) uint8_t ring0[C::STAGE];
@@ -191,333 +215,88 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
   };
   const lds_f32* wscl = (const lds_f32*)wsc;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave % C::WN, wt = wave / C::WN;
-  const int kbs = a.k_dim / kKB;
-  const int nblk_w = a.n_rows / 128;
-  const int total_m = __builtin_amdgcn_readfirstlane((int)a.hdr[kHdrMTiles]);
-  const int64_t total = (int64_t)total_m * a.n_tiles;
-  const int xcd = blockIdx.x & 7;
-  const int slot = blockIdx.x >> 3;
-  const int per_xcd = gridDim.x >> 3;
-  const int64_t v_begin = total * xcd / 8, v_end = total * (xcd + 1) / 8;
-  // lane's offset of its first weight block and (two halves of) token block
-  const uint32_t a_lane = (uint32_t)(wn * (C::G / 16)) * 2048u + (uint32_t)lane * 16u;
-  const int tl = lane & 15;
-  const uint32_t b_lane0 = (uint32_t)(wt * C::TBW) * 2048u + 16u * (uint32_t)(8 * tl + ((2 * (lane >> 4)) ^ tok_swz(tl)));
-  const uint32_t b_lane1 =
-      (uint32_t)(wt * C::TBW) * 2048u + 16u * (uint32_t)(8 * tl + ((2 * (lane >> 4) + 1) ^ tok_swz(tl)));
-  const int t_lane = wt * C::TW + tl;  // token of this lane's outputs in token block 0
-  // Promotion role: thread (pb, pt) keeps the running scale product
-  // F = sx[pt] * sw[pb] of weight block pb (gate / first 128 rows or up /
-  // second) for token pt, and publishes r = F_prev / F_next per K-block.
-  const bool prole = tid < 2 * BT;
-  const int pt = tid % BT, pb = (tid / BT) & 1;
+#include "moe_gemm_fp8_body.inc"
+}
 
-  // ---- tile state -----------------------------------------------------------
-  // Coordinates and per-lane DMA sources of the tile whose loads are in
-  // flight.  They are set one tile ahead: the next tile's first stages are
-  // issued before the current tile's epilogue, which then hides their latency.
-  int e = 0, p0 = 0, rows_valid = 1, nt = 0, mt = 0, m0 = 0, gm = 1, nb0 = 0, nb1 = 0, pf_lanes = 8;
-  const uint8_t* a_src = a.w;
-  const uint8_t* b_src[C::B_INSTR];
-  const float* s_src = a.a_scale;
-  const uint8_t* pf_src = a.w;
-  auto src_row = [&](int t) -> int64_t {
-    const int p = p0 + min(t, rows_valid - 1);
-    if (!FC1) return p;
-    const int r = a.sorted_route[p];
-    return a.a_mode == 2 ? r : r / a.top_k;
+// FC1 then FC2 in one launch: each workgroup runs its FC1 tiles, then its
+// FC2 tiles, each of which first waits for its row tile's FC1 rows.  A
+// cooperative launch (every workgroup resident, or the launch fails): a
+// waiting workgroup only waits for FC1 tiles, which belong to resident
+// workgroups and never wait themselves, so every wait ends.
+template <int BT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_fp8_persist_kernel(GemmArgs a1, GemmArgs a2, PersistArgs q) {
+  using C = Cfg<BT>;
+  constexpr bool PERSIST = true;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring2[C::STAGES > 2 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring3[C::STAGES > 3 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) float wsc[2 * kMaxKBlocks];
+  __shared__ __attribute__((aligned(16))) float sx0[BT];
+  __shared__ __attribute__((aligned(16))) float rsc[2][BT][2];
+  __shared__ __attribute__((aligned(16))) float fsc[BT][2];
+  __shared__ __attribute__((aligned(16))) uint32_t l2sink[kThreads];
+  __shared__ __attribute__((aligned(16))) float red_s[C::WN * BT];
+  __shared__ int32_t cb_list[BT];
+  __shared__ int32_t cb_count;
+  auto ring = [&](auto stage) -> lds_u8* {
+    constexpr int S = decltype(stage)::value;
+    if constexpr (S == 0) return (lds_u8*)ring0;
+    else if constexpr (S == 1) return (lds_u8*)ring1;
+    else if constexpr (S == 2) return (lds_u8*)ring2;
+    else return (lds_u8*)ring3;
   };
-  auto setup = [&](int64_t v) {
-    const int64_t group = v / ((int64_t)kGroupM * a.n_tiles);
-    const int64_t rem = v - group * kGroupM * a.n_tiles;
-    m0 = (int)(group * kGroupM);
-    gm = min(kGroupM, total_m - m0);
-    nt = (int)(rem / gm);
-    mt = m0 + (int)(rem % gm);
-    // tile scalars are wave-uniform; saying so keeps their dependents
-    // (weight-scale addresses) on the scalar unit
-    e = __builtin_amdgcn_readfirstlane(a.tiles[2 * mt]);
-    p0 = __builtin_amdgcn_readfirstlane(a.tiles[2 * mt + 1]);
-    rows_valid = min(BT, __builtin_amdgcn_readfirstlane(a.offsets[e + 1]) - p0);
-    if (FC1) {
-      nb0 = nt;                  // gate block
-      nb1 = a.inter / 128 + nt;  // up block
-    } else {
-      nb0 = 2 * nt;
-      nb1 = min(2 * nt + 1, nblk_w - 1);
-    }
-    // weights: the tile's K-blocks are contiguous 32 KB pieces
-    a_src = a.w + ((int64_t)e * a.n_tiles + nt) * kbs * (int64_t)C::A_BYTES + (wave * C::A_INSTR * 64 + lane) * 16;
-    // tokens: LDS position V (16 bytes) of the stage holds chunk
-    // (V % 8) ^ tok_swz(token) of token V / 8 (see tok_swz)
-#pragma unroll
-    for (int j = 0; j < C::B_INSTR; ++j) {
-      const int v8 = wave * BT + j * 64 + (lane < C::B_LANES ? lane : 0);
-      const int t = v8 >> 3;
-      const int chunk = (v8 & 7) ^ tok_swz(t & 15);
-      b_src[j] = a.a + src_row(t) * a.k_dim + chunk * 16;
-    }
-    // token scales: a stage carries those of the next K-block (the promotion
-    // threads turn them into ratios one K-block ahead of their use)
-    s_src = a.a_scale + src_row(wave * C::S_LANES + (lane < C::S_LANES ? lane : 0)) * kbs;
-    // L2 prefetch of weights kPrefetchAhead K-blocks ahead of the stage
-    // being loaded: the gm token tiles of a group share this weight tile
-    // (they run side by side on one XCD), so each prefetches every gm-th of
-    // its 256 lines; one word per line lands in l2sink.  Weight K-blocks are
-    // first touches (the token rows are L2 hits by then), and a stage waits
-    // for its slowest load.
-    pf_lanes = 32 / gm;  // lines per wave per K-block
-    const int pf_line = (wave * pf_lanes + (lane < pf_lanes ? lane : 0)) * gm + (mt - m0);
-    pf_src = a.w + ((int64_t)e * a.n_tiles + nt) * kbs * (int64_t)C::A_BYTES + pf_line * 128;
-  };
-
-  auto issue = [&](auto stage, int kb) {
-    const lds_u8* As = ring(stage);
-    const lds_u8* Bs = As + C::A_BYTES;
-    const lds_u8* Ss = Bs + C::B_BYTES;
-#pragma unroll
-    for (int j = 0; j < C::A_INSTR; ++j)
-      dma16(a_src + (int64_t)kb * C::A_BYTES + j * 1024, As + (wave * C::A_INSTR + j) * 1024);
-#pragma unroll
-    for (int j = 0; j < C::B_INSTR; ++j)
-      if (lane < C::B_LANES) dma16(b_src[j] + kb * kKB, Bs + (wave * BT + j * 64) * 16);
-    if (lane < C::S_LANES) dma4(s_src + min(kb + 1, kbs - 1), Ss + wave * C::S_LANES * 4);
-    if (lane < pf_lanes)
-      dma4(reinterpret_cast<const float*>(pf_src + (int64_t)min(kb + kPrefetchAhead, kbs - 1) * C::A_BYTES),
-           (const lds_u8*)l2sink + wave * 256);
-  };
-
-  // The loads a tile needs before its first step: its two weight-scale
-  // columns (waves 0-3), the token scales of K-block 0 and the first
-  // STAGES - 1 stages.  The scale loads are older than every stage load, so
-  // the first stage's wait covers them.
-  auto prologue = [&]() {
-    if (wave < 4) {
-      const int blk = wave >> 1, half = wave & 1;
-      const int kb = half * 64 + lane;
-      if (kb < kbs)
-        dma4(a.w_scale + ((int64_t)e * nblk_w + (blk ? nb1 : nb0)) * kbs + kb,
-             (const lds_u8*)wsc + (blk * kMaxKBlocks + half * 64) * 4);
-    }
-    if (lane < C::S_LANES) dma4(s_src, (const lds_u8*)sx0 + wave * C::S_LANES * 4);
-    // K-block 0 meets a zero accumulator: any finite ratio will do
-    if (prole) rsc[0][pt][pb] = 0.0f;
-    issue(std::integral_constant<int, 0>{}, 0);
-    if (C::STAGES > 2 && 1 < kbs) issue(std::integral_constant<int, 1>{}, 1);
-    if (C::STAGES > 3 && 2 < kbs) issue(std::integral_constant<int, (C::STAGES > 3 ? 2 : 0)>{}, 2);
-  };
-
-  int64_t v = v_begin + slot;
-  if (v < v_end) {
-    setup(v);
-    prologue();
+  const lds_f32* wscl = (const lds_f32*)wsc;
+  {
+    constexpr bool FC1 = true;
+    const GemmArgs& a = a1;
+#include "moe_gemm_fp8_body.inc"
   }
-  if constexpr (!FC1) {
-    if (a.fc.out) zero_unrouted_rows(a.fc, (int)a.hdr[kHdrTokens], a.top_k, a.n_rows);
+  __syncthreads();  // the FC2 phase's first loads reuse the LDS the last FC1 epilogue read
+  {
+    constexpr bool FC1 = false;
+    const GemmArgs& a = a2;
+#include "moe_gemm_fp8_body.inc"
   }
-  for (; v < v_end; v += per_xcd) {
-    float pf = 1.0f;
-    v4f acc[C::NB][C::TBW];
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-      for (int tb = 0; tb < C::TBW; ++tb) acc[nb][tb] = v4f{0.f, 0.f, 0.f, 0.f};
+}
 
-    // ---- K loop: STAGES-deep LDS ring -------------------------------------
-    // acc holds sum_{j <= kb} P_j * F_j / F_kb for block products P_j; before
-    // block kb's MFMAs it is rescaled by r_kb = F_{kb-1} / F_kb, and after the
-    // loop multiplied by F_last.
-    auto step = [&](auto stage, int kb) {
-      constexpr int ST = decltype(stage)::value;
-      const int ahead = min(C::STAGES - 2, kbs - 1 - kb);  // stages issued after this one
-      if (C::STAGES >= 4 && ahead >= 2) wait_vmcnt<(C::STAGES >= 4 ? 2 : 0) * C::N_LD>();
-      else if (C::STAGES >= 3 && ahead >= 1) wait_vmcnt<(C::STAGES >= 3 ? 1 : 0) * C::N_LD>();
-      else wait_vmcnt<0>();
-      // Every wave has its own DMA for this stage complete and its ratio
-      // writes of the previous step done; the barrier makes that true for
-      // all waves.  It also orders the previous stage's LDS reads (consumed
-      // by MFMAs already) before the DMA issued next into it.  A plain
-      // s_barrier: a fenced barrier would also drain the DMA of the stages
-      // still in flight.
-      wait_lgkmcnt0();
-      barrier_nofence();
-      if (kb + C::STAGES - 1 < kbs)
-        issue(std::integral_constant<int, (ST + C::STAGES - 1) % C::STAGES>{}, kb + C::STAGES - 1);
+template <int BT>
+static int launch_persist(const GemmArgs& a1, const GemmArgs& a2, const PersistArgs& q, int grid, void* stream) {
+  GemmArgs x1 = a1, x2 = a2;
+  PersistArgs xq = q;
+  void* args[] = {&x1, &x2, &xq};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&gemm_fp8_persist_kernel<BT>), dim3(grid),
+                                    dim3(kThreads), args, 0, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? 0
+             : -1;
+}
 
-      const lds_u8* As = ring(stage);
-      const lds_u8* Bs = As + C::A_BYTES;
-      const lds_f32* Ss = (const lds_f32*)(Bs + C::B_BYTES);
-      const lds_u8* Ap = As + a_lane;
-      const lds_u8* Bp0 = Bs + b_lane0;
-      const lds_u8* Bp1 = Bs + b_lane1;
-      typedef __attribute__((address_space(3))) const v2f lds_v2f;
-      const lds_v2f* Rp = (const lds_v2f*)((const lds_f32*)&rsc[kb & 1][0][0] + 2 * t_lane);
-      auto aoff = [](int nb) {  // byte offset of weight block nb of this wave
-        return (nb < C::NB / 2 ? nb : 8 - C::NB / 2 + nb) * 2048;
-      };
-      if constexpr (C::NB > C::TBW) {
-        // Hold the token fragments; weight fragments stream one block ahead.
-        // The scheduling barrier keeps the compiler from hoisting every
-        // block's LDS reads to the top (all of them live at once).
-        v8i bq[C::TBW];
-        v2f rr[C::TBW];
-#pragma unroll
-        for (int tb = 0; tb < C::TBW; ++tb) {
-          bq[tb] = lds_frag2(Bp0 + tb * 2048, Bp1 + tb * 2048);
-          rr[tb] = Rp[tb * 16];
-        }
-        v8i aq = lds_frag(Ap + aoff(0));
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
-          const v8i an = lds_frag(Ap + aoff(nb + 1 < C::NB ? nb + 1 : nb));
-#pragma unroll
-          for (int tb = 0; tb < C::TBW; ++tb)
-            acc[nb][tb] = mfma_fp8(aq, bq[tb], acc[nb][tb] * (nb < C::NB / 2 ? rr[tb].x : rr[tb].y));
-          __builtin_amdgcn_sched_barrier(0);
-          aq = an;
-        }
-      } else {
-        // Hold the weight fragments; token fragments stream one block ahead.
-        v8i aq[C::NB];
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) aq[nb] = lds_frag(Ap + aoff(nb));
-        v8i bq = lds_frag2(Bp0, Bp1);
-        v2f rr = Rp[0];
-#pragma unroll
-        for (int tb = 0; tb < C::TBW; ++tb) {
-          const int tn = tb + 1 < C::TBW ? tb + 1 : tb;
-          const v8i bn = lds_frag2(Bp0 + tn * 2048, Bp1 + tn * 2048);
-          const v2f rn = Rp[tn * 16];
-#pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb) acc[nb][tb] = mfma_fp8(aq[nb], bq, acc[nb][tb] * (nb < C::NB / 2 ? rr.x : rr.y));
-          __builtin_amdgcn_sched_barrier(0);
-          bq = bn;
-          rr = rn;
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // promotion threads: ratios of K-block kb + 1 (read by every wave at
-      // the next step)
-      if (prole) {
-        const float swb_kb = wscl[pb * kMaxKBlocks + kb];
-        if (kb == 0) pf = carry_scale(((const lds_f32*)sx0)[pt] * swb_kb, 1.0f);
-        if (kb + 1 < kbs) {
-          const float fn = carry_scale(Ss[pt] * wscl[pb * kMaxKBlocks + kb + 1], pf);
-          rsc[(kb + 1) & 1][pt][pb] = pf * __builtin_amdgcn_rcpf(fn);
-          pf = fn;
-        }
-      }
-    };
-    for (int kb = 0; kb < kbs; kb += C::STAGES) {
-      step(std::integral_constant<int, 0>{}, kb);
-      if (kb + 1 < kbs) step(std::integral_constant<int, 1>{}, kb + 1);
-      if (C::STAGES > 2 && kb + 2 < kbs) step(std::integral_constant<int, (C::STAGES > 2 ? 2 : 0)>{}, kb + 2);
-      if (C::STAGES > 3 && kb + 3 < kbs) step(std::integral_constant<int, (C::STAGES > 3 ? 3 : 0)>{}, kb + 3);
-    }
-    if (prole) fsc[pt][pb] = pf;
-    __syncthreads();  // every wave is done with the ring (and fsc is visible) before the epilogue
-    // this tile's epilogue coordinates; then the next tile's first loads
-    const int ep_p0 = p0, ep_rows = rows_valid, ep_nt = nt;
-    if (v + per_xcd < v_end) {
-      setup(v + per_xcd);
-      prologue();
-    }
-    // undo the running scale: acc = sum_kb F_kb * (block product)
-#pragma unroll
-    for (int tb = 0; tb < C::TBW; ++tb) {
-      const v2f f = ((const __attribute__((address_space(3))) v2f*)((const lds_f32*)&fsc[0][0]))[t_lane + tb * 16];
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) acc[nb][tb] *= (nb < C::NB / 2 ? f.x : f.y);
-    }
+int launch_fc1_fc2(const GemmArgs& a1, const GemmArgs& a2, const PersistArgs& q, int block_m, int grid, void* stream) {
+  switch (block_m) {
+    case 16: return launch_persist<16>(a1, a2, q, grid, stream);
+    case 32: return launch_persist<32>(a1, a2, q, grid, stream);
+    case 64: return launch_persist<64>(a1, a2, q, grid, stream);
+    case 128: return launch_persist<128>(a1, a2, q, grid, stream);
+    case 256: return launch_persist<256>(a1, a2, q, grid, stream);
+  }
+  return -1;
+}
 
-    // ---- epilogue -----------------------------------------------------------
-    if (FC1 && a.gateup != nullptr) {
-      // unfused FC1: FP32 gate and up rows, SwiGLU + requant run separately
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) {
-        const int col = (nb < C::NB / 2 ? 0 : a.inter) + ep_nt * 128 + wn * C::G + (nb % (C::NB / 2)) * 16 + 4 * (lane >> 4);
-#pragma unroll
-        for (int tb = 0; tb < C::TBW; ++tb) {
-          const int t = wt * C::TW + tb * 16 + (lane & 15);
-          if (t < ep_rows) *reinterpret_cast<v4f*>(a.gateup + (int64_t)(ep_p0 + t) * (2 * a.inter) + col) = acc[nb][tb];
-        }
-      }
-    } else if (FC1) {
-      // h = silu(gate) * up = g / (1 + 2^(-g log2 e)) * up on the hardware
-      // exp2 and reciprocal; then the 1x128 amax, s = amax / 448 and the
-      // codes of h * (1 / s).
-      float* red = red_s;  // [WN][BT] partial amax
-      float hv[C::TBW][C::NB / 2][4];
-#pragma unroll
-      for (int tb = 0; tb < C::TBW; ++tb) {
-        float m = 0.f;
-#pragma unroll
-        for (int g = 0; g < C::NB / 2; ++g)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float gt = acc[g][tb][i], up = acc[C::NB / 2 + g][tb][i];
-            const float h = swiglu(gt, up);
-            hv[tb][g][i] = h;
-            m = fmaxf(m, fabsf(h));
-          }
-        m = fmaxf(m, __shfl_xor(m, 16));
-        m = fmaxf(m, __shfl_xor(m, 32));
-        if (lane < 16) red[wn * BT + wt * C::TW + tb * 16 + lane] = m;
-      }
-      // LDS-only exchange: a fenced barrier would also wait for the next
-      // tile's loads issued above
-      wait_lgkmcnt0();
-      barrier_nofence();
-      const int ikb = a.inter / 128;
-#pragma unroll
-      for (int tb = 0; tb < C::TBW; ++tb) {
-        const int t = wt * C::TW + tb * 16 + (lane & 15);
-        float amax = 0.f;
-#pragma unroll
-        for (int w = 0; w < C::WN; ++w) amax = fmaxf(amax, red[w * BT + t]);
-        const float s = amax / kE4m3Max;
-        const float inv = requant_inv(amax, s);
-        if (t < ep_rows) {
-          uint8_t* dst = a.hq + (int64_t)(ep_p0 + t) * a.inter + ep_nt * 128 + wn * C::G + 4 * (lane >> 4);
-#pragma unroll
-          for (int g = 0; g < C::NB / 2; ++g) {
-            int w = cvt2_e4m3(hv[tb][g][0] * inv, hv[tb][g][1] * inv, 0, false);
-            w = cvt2_e4m3(hv[tb][g][2] * inv, hv[tb][g][3] * inv, w, true);
-            *reinterpret_cast<uint32_t*>(dst + g * 16) = (uint32_t)w;
-          }
-          if (wn == 0 && (lane >> 4) == 0) a.hs[(int64_t)(ep_p0 + t) * ikb + ep_nt] = s;
-        }
-      }
-    } else {
-      const int n0 = ep_nt * kBN;
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) {
-        const int n = (nb < C::NB / 2 ? wn * C::G + nb * 16 : 128 + wn * C::G + (nb - C::NB / 2) * 16) +
-                      4 * (lane >> 4);
-#pragma unroll
-        for (int tb = 0; tb < C::TBW; ++tb) {
-          const int t = wt * C::TW + tb * 16 + (lane & 15);
-          if (t < ep_rows && n0 + n < a.n_rows) {
-            u32x2 o;
-            o[0] = f32_to_bf16_rne(acc[nb][tb][0]) | (f32_to_bf16_rne(acc[nb][tb][1]) << 16);
-            o[1] = f32_to_bf16_rne(acc[nb][tb][2]) | (f32_to_bf16_rne(acc[nb][tb][3]) << 16);
-            uint16_t* dst = a.y + (int64_t)(ep_p0 + t) * a.n_rows + n0 + n;
-            if (a.fc.out)
-              store_y_coherent(dst, o[0], o[1]);  // read by the workgroup that completes the token
-            else
-              *reinterpret_cast<u32x2*>(dst) = o;
-          }
-        }
-      }
-      if (a.fc.out)
-        arrive_and_combine<kThreads>(a.fc, a.y, a.sorted_route, a.top_k, a.n_rows, a.n_tiles, ep_p0, ep_rows, ep_nt,
-                                     (__attribute__((address_space(3))) int32_t*)cb_list,
-                                     (__attribute__((address_space(3))) int32_t*)&cb_count);
-    }
+template <int BT>
+static int occ_persist() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_fp8_persist_kernel<BT>, kThreads, 0) != hipSuccess)
+    return 1;
+  return n > 0 ? n : 1;
+}
+
+int gemm_persist_max_workgroups_per_cu(int block_m) {
+  switch (block_m) {
+    case 16: return occ_persist<16>();
+    case 32: return occ_persist<32>();
+    case 64: return occ_persist<64>();
+    case 128: return occ_persist<128>();
+    default: return occ_persist<256>();
   }
 }
 

@@ -12,8 +12,8 @@ namespace moe {
 constexpr int kMaxExperts = 1024;
 constexpr int kCompactChunk = 4096;  // routes per compaction workgroup (256 lanes x 16)
 constexpr int kFuseRoutes = 2048;    // staging and compaction share one launch up to this many routes
-constexpr int kNumRegions = 20;
-constexpr int kRegionBlkBase = 19;   // internal: per-(compaction block, expert) bases
+constexpr int kNumRegions = 21;
+constexpr int kRegionBlkBase = 20;   // internal: per-(compaction block, expert) bases
 
 // Words of the device header (MOE_REGION_STATUS).
 enum HeaderWord : int {
@@ -86,6 +86,7 @@ struct CompactArgs {
   int32_t* sorted_route;   // [row_cap]
   int32_t* route_pos;      // [routes]
   int32_t* tiles;          // [max_m_tiles, 2]
+  int32_t* ready;          // [max_m_tiles] persistent FC1->FC2 counters, zeroed per listed tile (or null)
 };
 int launch_compact(const CompactArgs& a, void* stream);
 // Stage and compact in one launch (routes <= kCompactChunk).
@@ -125,6 +126,18 @@ struct GemmArgs {
   FusedCombineArgs fc;     // FC2: last-arriver combine into the output (fc.out null: none)
 };
 int launch_fc1(const GemmArgs& a, int block_m, void* stream);
+
+// FC1 then FC2 in one persistent cooperative launch (MOE_FLAG_PERSISTENT_FFN).
+// FC1 row tile m counts its finished column tiles in ready[m]; an FC2 tile
+// of row tile m starts once ready[m] == need.  A wait longer than the spin
+// bound sets MOE_DEV_WAIT_TIMEOUT in *status and goes on.
+struct PersistArgs {
+  int32_t* ready;    // [max_m_tiles], zeroed by the compaction for the tiles it lists
+  int32_t need;      // FC1 column tiles per row tile (I / 128)
+  uint32_t* status;  // device status word (MOE_DEV_* bits)
+};
+int launch_fc1_fc2(const GemmArgs& a1, const GemmArgs& a2, const PersistArgs& q, int block_m, int grid, void* stream);
+int gemm_persist_max_workgroups_per_cu(int block_m);
 // Unfused FC1 second half: SwiGLU + 1x128 requant of the FP32 gate/up rows.
 int launch_swiglu_quant(const float* gateup, int32_t row_cap, int32_t inter, const uint32_t* hdr, uint8_t* hq,
                         float* hs, void* stream);

@@ -175,5 +175,20 @@ def test_fused_combine_flag():
                                         flags=L.MOE_FLAG_FUSED_COMBINE), 128, 4096, 1.0)
     assert mx_fus - mx_base == 4096 * 28 * 4
     with pytest.raises(L.MoEError) as ei:
-        L.moe_workspace_query(_cfg(flags=16), 128, 4096, 1.0)
+        L.moe_workspace_query(_cfg(flags=32), 128, 4096, 1.0)
     assert ei.value.status == L.MOE_ERR_INVALID_ARG
+
+
+def test_persistent_ffn_flag():
+    """MOE_FLAG_PERSISTENT_FFN adds one int32 readiness counter per row tile
+    (max_m_tiles of them) and is an FP8-path option without the unfused FC1."""
+    base = L.moe_workspace_query(_cfg(), 128, 4096, 1.0)
+    per = L.moe_workspace_query(_cfg(flags=L.MOE_FLAG_CHECK_ROUTES | L.MOE_FLAG_PERSISTENT_FFN), 128, 4096, 1.0)
+    max_m_tiles = (4096 * 8 + 127) // 128 + 32  # row_cap / block_m rounded up, plus one per expert
+    assert per - base == (max_m_tiles * 4 + 255) // 256 * 256
+    for kw in (dict(weight_format=L.MOE_WEIGHT_MXFP8_E4M3, act_format=L.MOE_ACT_BF16,
+                    flags=L.MOE_FLAG_PERSISTENT_FFN),
+               dict(flags=L.MOE_FLAG_PERSISTENT_FFN | L.MOE_FLAG_UNFUSED_FC1)):
+        with pytest.raises(L.MoEError) as ei:
+            L.moe_workspace_query(_cfg(**kw), 128, 4096, 1.0)
+        assert ei.value.status == L.MOE_ERR_UNSUPPORTED
