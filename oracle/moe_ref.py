@@ -69,9 +69,17 @@ STATUS_CAPACITY = 8
 
 PIN_STATUS = {
     "formats.e4m3_decode": "pinned: exhaustive vs OCP bit-field values and torch.float8_e4m3fn",
+    "formats.e5m2_decode": "pinned: exhaustive vs OCP bit-field values and torch.float8_e5m2",
+    "formats.bf16_bits_to_f64": "pinned: round trips of the bfloat16 rounding tests (exact widening)",
     "formats.e8m0_decode": "pinned: exhaustive vs torch.float8_e8m0fnu",
     "formats.e4m3_encode_rne_sat": "pinned: all midpoints +-1 ulp and random values vs torch cast",
     "formats.bf16_rne_bits": "pinned: vs torch bfloat16 cast (float32 inputs) and exact fractions",
+    "dequant_block128": "pinned: exact-rational FC1 and one-hot FC1/FC2 closed forms recompute it",
+    "dequant_rows_1x128": "pinned: exact-rational FC1 recomputes it from the codes and scales",
+    "dequant_mx": "pinned: one-hot MX closed form and the per-route loop recompute 2^(e-127) scaling",
+    "silu": "pinned: one-hot SwiGLU closed form g/(1+exp(-g))*u",
+    "requant_1x128": "pinned: requantisation invariants (scale = amax/448, a code at 448, error bound)",
+    "fc1_gateup": "pinned: exact rational (fractions) on the tiny shape, one-hot closed form",
     "stage_quantize_1x128": "pinned: torch-cast cross-check, amax->448 invariant, error bound",
     "stage_routes": "pinned: brute-force loops and masked-route semantics",
     "compact": "pinned: brute-force loops",

@@ -259,3 +259,17 @@ def test_page_figure_fused_fc1_buffer():
     fig = _page_figures()
     ep, capacity, k, two_i = 8, 2048, 8, 2 * CONFIGS["dsv3"].intermediate
     assert ep * capacity * k * two_i * 2 == fig["fused_fc1_bytes"]
+
+
+def test_every_oracle_function_has_a_pin():
+    """Every public function of the oracle names the pin that holds it."""
+    import inspect
+
+    from oracle import formats as OF
+    for mod, prefix in ((M, ""), (OF, "formats.")):
+        for name, fn in inspect.getmembers(mod, inspect.isfunction):
+            if name.startswith("_") or fn.__module__ != mod.__name__:
+                continue
+            key = prefix + name
+            assert key in M.PIN_STATUS, f"{key} has no PIN_STATUS entry"
+            assert M.PIN_STATUS[key].startswith("pinned:"), key
