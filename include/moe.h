@@ -10,6 +10,9 @@
  *   -> FC2 (FP8 block-scale grouped GEMM)
  *   -> owner-side FP32 weighted top-k combine to a BF16 output.
  *
+ * Optional forms of the same arithmetic (cfg->flags): the unfused FC1, the
+ * combine fused into FC2, and FC1 + FC2 in one persistent launch.
+ *
  * This is the forward pipeline in the Description of "feat(moe_ep): add SM90
  * push FP8 mega-MoE backend for Hopper" (flashinfer PR #4069) with its
  * cross-GPU steps (tags, acks, peer dispatch, prefix waits) removed, the
@@ -27,7 +30,9 @@
  *    before anything is launched; moe_last_error() then describes it.
  *  - Problems found on the device (bad routes, capacity overflow) never
  *    abort: the offending routes are masked and a bit is set in the device
- *    status word, read with moe_read_status().
+ *    status word, read with moe_read_status().  Every wait inside a kernel
+ *    is bounded; one that gives up sets MOE_DEV_WAIT_TIMEOUT instead of
+ *    hanging.
  *  - Calls on one layer handle are not thread-safe; distinct handles with
  *    distinct workspaces are independent.
  */

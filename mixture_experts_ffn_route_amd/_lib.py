@@ -2,8 +2,9 @@
 
 Every function here has the name of the C entry point it wraps, takes plain
 integers (device pointers as ``int``) and raises ``MoEError`` for a negative
-status.  The shared library must have been built (``build.py``); importing
-this module without it raises ``ImportError`` -- there is no fallback.
+status.  The shared library is loaded as built (``build.py``); when none has
+been built, it is compiled once from the HIP sources first.  If that fails,
+importing this module raises ``ImportError`` -- there is no fallback.
 """
 
 from __future__ import annotations
@@ -83,7 +84,12 @@ class moe_tactic_t(Structure):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"HIP library {LIB_PATH} is not built; run __graft_entry__.build()")
+        # nothing built yet: compile the gfx950 library (hipcc), else fail
+        try:
+            from . import build as _build
+            _build.build()
+        except Exception as exc:  # noqa: BLE001
+            raise ImportError(f"HIP library {LIB_PATH} is not built and building it failed: {exc}") from exc
     # One HIP runtime per process: torch ships its own libamdhip64 (SONAME
     # libamdhip64.so.7).  Loading torch first makes the dynamic linker bind
     # this library to that same runtime, so torch's streams and allocations
