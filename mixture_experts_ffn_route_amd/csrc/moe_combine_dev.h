@@ -83,7 +83,7 @@ __device__ __forceinline__ void combine8_k(const uint16_t* y, const int32_t* rou
   }
   cb_u32x4 o;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16_rne(acc[2 * i]) | (f32_to_bf16_rne(acc[2 * i + 1]) << 16);
+  for (int i = 0; i < 4; ++i) o[i] = bf16x2_rne(acc[2 * i], acc[2 * i + 1]);
   *reinterpret_cast<cb_u32x4*>(out + t * hidden + c) = o;
 }
 

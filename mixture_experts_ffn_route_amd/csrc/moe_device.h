@@ -11,13 +11,18 @@ constexpr float kE4m3Max = 448.0f;
 // bfloat16 bits -> float (exact).
 __device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
-// float -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two floats -> two bfloat16 in one word (a in the low half), round to
+// nearest even, on the gfx950 packed conversion (v_cvt_pk_bf16_f32).  It
+// matches the bit-field rounding (add 0x7fff plus the kept LSB, NaN made
+// quiet) on every float tested, ties and NaNs included.
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
+
+// float -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) { return bf16x2_rne(f, 0.0f) & 0xffffu; }
 
 // Two floats -> two e4m3 codes in the low (hi=false) or high (hi=true) 16
 // bits of `old`.  The hardware conversion rounds to nearest even; inputs are

@@ -348,8 +348,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
           const int t = wt * C::TW + tb * 16 + (lane & 15);
           if (t < rows_valid && n0 + n < a.n_rows) {
             u32x2 o;
-            o[0] = f32_to_bf16_rne(acc[nb][tb][0]) | (f32_to_bf16_rne(acc[nb][tb][1]) << 16);
-            o[1] = f32_to_bf16_rne(acc[nb][tb][2]) | (f32_to_bf16_rne(acc[nb][tb][3]) << 16);
+            o[0] = bf16x2_rne(acc[nb][tb][0], acc[nb][tb][1]);
+            o[1] = bf16x2_rne(acc[nb][tb][2], acc[nb][tb][3]);
             uint16_t* dst = a.y + (int64_t)(p0 + t) * a.n_rows + n0 + n;
             if (a.fc.out)
               store_y_coherent(dst, o[0], o[1]);  // read by the workgroup that completes the token
