@@ -63,6 +63,8 @@ def workload_bytes(shape, counts, tokens, with_stage=True, mx=False):
 # file records a hash of the sources that decide the FC1 kernel and its launch.
 COUNTER_FILE = os.path.join(ROOT, "profiles", "fc1_dsv3_T4096_hbm_counters.txt")
 COUNTER_SOURCES = ["mixture_experts_ffn_route_amd/csrc/moe_gemm_fp8.hip",
+                   "mixture_experts_ffn_route_amd/csrc/moe_gemm_fp8_body.inc",
+                   "mixture_experts_ffn_route_amd/csrc/moe_device.h",
                    "mixture_experts_ffn_route_amd/csrc/moe_host.cpp",
                    "mixture_experts_ffn_route_amd/csrc/moe_api.cpp"]
 
