@@ -211,6 +211,10 @@ typedef struct moe_layer moe_layer_t;
  *  capacity_factor route rows held = ceil(capacity_factor * max_rows * K),
  *                  capped at max_rows*K; 1.0 never drops a route.
  *  ws_bytes        [host out] bytes, a multiple of 256.
+ * MOE_ERR_UNSUPPORTED when, with E4M3_BLOCK128 weights, the staged
+ * activations (max_rows * H bytes, max_rows * K * H with per-route staging)
+ * or the FC1 output (route rows held * I bytes) reach 2 GiB: the FP8 GEMMs
+ * address them with 31-bit offsets.
  * The split between tactic (expected_m) and memory bound (max_rows,
  * capacity_factor) is the workspace contract of PR #4069 ("Contracts
  * introduced by this PR": capacity_factor bounds the GEMM and scale buffers;

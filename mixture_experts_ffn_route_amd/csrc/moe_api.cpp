@@ -147,6 +147,8 @@ extern "C" moe_status_t moe_layer_create(const moe_config_t* cfg, int32_t expect
     return moe::fail(MOE_ERR_INVALID_ARG, "workspace must be non-NULL and 256-byte aligned");
   moe::Tactic t = moe::choose_tactic(*cfg, expected_m);
   moe::Layout L = moe::compute_layout(*cfg, t, max_rows, capacity_factor);
+  s = moe::validate_layout(*cfg, L);
+  if (s != MOE_OK) return s;
   if (ws_bytes < L.total)
     return moe::fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < required %zu", ws_bytes, L.total);
 

@@ -121,31 +121,68 @@ __device__ __forceinline__ v8i lds_frag2(const lds_u8* lo_p, const lds_u8* hi_p)
 // on the vector-memory counter itself.  The "memory" clobber keeps every LDS
 // access in program order around these instructions.
 __device__ __forceinline__ uint32_t lds_addr(const lds_u8* p) { return (uint32_t)(uintptr_t)p; }
-__device__ __forceinline__ void dma16(const uint8_t* src, const lds_u8* lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
-}
 __device__ __forceinline__ void dma4(const float* src, const lds_u8* lds_wave_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                :: "v"(src), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
+}
+
+// The same loads from a wave-uniform base (an SGPR pair) plus a 32-bit
+// per-lane byte offset: the K loop keeps one 32-bit VGPR per gathered
+// address instead of a 64-bit pointer.  No instruction offset: on these
+// loads it would move the LDS destination as well as the source.
+__device__ __forceinline__ void dma16o(const void* base, uint32_t off, const lds_u8* lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(base), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4o(const void* base, uint32_t off, const lds_u8* lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(off), "s"(base), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
 }
 
 // Scale loads of the persistent FC2 phase read rows that FC1 tiles on other
 // XCDs have just written, and two rows share a cache line, so they are made
 // at agent scope (sc1) instead of from a possibly stale L2 line.
 template <bool kCoherent>
-__device__ __forceinline__ void dma4_scale(const float* src, const lds_u8* lds_wave_base) {
+__device__ __forceinline__ void dma4o_scale(const void* base, uint32_t off, const lds_u8* lds_wave_base) {
   if constexpr (kCoherent)
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off sc1"
-                 :: "v"(src), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1 sc1"
+                 :: "v"(off), "s"(base), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
   else
-    dma4(src, lds_wave_base);
+    dma4o(base, off, lds_wave_base);
 }
 
 // Write-through store (agent scope) of h codes and scales in the persistent
 // launch, where FC2 tiles on other XCDs read them within the same kernel.
 __device__ __forceinline__ void store_wt_u32(uint8_t* p, uint32_t v) {
   __hip_atomic_store(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Raw buffer stores (gfx9 buffer resource: base, stride 0, num_records,
+// word 3 = 32-bit data format, no swizzle).  A store whose VGPR offset lies
+// past num_records is dropped by the hardware (the SGPR offset is not part
+// of that check, so it stays 0 here), so a store can be issued by every lane
+// with the masked lanes out of range.  Written as volatile asm so the
+// compiler neither merges nor removes any: the K loop's waits count them.
+constexpr uint32_t kBufferRsrcWord3 = 0x00020000u;
+// `base` and `num_records` are wave-uniform; readfirstlane says so, so the
+// descriptor sits in SGPRs as the instruction requires.
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t num_records) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b),
+               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xffffu),
+               (uint32_t)__builtin_amdgcn_readfirstlane(num_records), kBufferRsrcWord3};
+}
+// 8 bytes at base + voff + IMM (SGPR offset 0)
+template <int IMM>
+__device__ __forceinline__ void buffer_store8(u32x2 v, uint32_t voff, const u32x4& rsrc) {
+  static_assert(IMM >= 0 && IMM < 4096, "MUBUF offset field");
+  asm volatile("buffer_store_dwordx2 %0, %1, %2, 0 offen offset:%3"
+               :: "v"(v), "v"(voff), "s"(rsrc), "n"(IMM) : "memory");
+}
+// A store that writes nothing (an empty buffer): it only counts as an
+// outstanding vector-memory operation.
+__device__ __forceinline__ void buffer_store_none(const u32x4& empty_rsrc) {
+  asm volatile("buffer_store_dword %0, off, %1, 0" :: "v"(0u), "s"(empty_rsrc) : "memory");
 }
 
 // Polls of a readiness counter before a persistent FC2 tile gives up (each
@@ -184,7 +221,8 @@ struct Cfg {
   static constexpr int S_LANES = BT / kWaves;                     // scale loads per wave
   static constexpr int N_LD = A_INSTR + B_INSTR + 2;              // vector loads per wave per stage
   static_assert(TBW >= 1 && NB >= 2 && STAGES >= 2, "tile shape");
-  static_assert((STAGES - 2) * N_LD < 64, "vmcnt range");
+  static constexpr int EPI_STORES = NB * TBW;                     // FC2 output stores per wave per tile
+  static_assert((STAGES - 2) * N_LD + EPI_STORES < 64, "vmcnt range");
 };
 
 template <int BT, bool FC1>

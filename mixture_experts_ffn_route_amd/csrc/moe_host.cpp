@@ -96,6 +96,18 @@ Tactic choose_tactic(const moe_config_t& cfg, int32_t expected_m) {
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// The FP8 GEMMs gather token rows from the staged activations (FC1) and the
+// FC1 output (FC2) as 32-bit byte offsets from the buffer's base, kept
+// below 2^31 so that they read the same as signed or unsigned.
+moe_status_t validate_layout(const moe_config_t& cfg, const Layout& L) {
+  const size_t lim = (size_t)1 << 31;
+  if (cfg.weight_format == MOE_WEIGHT_E4M3_BLOCK128 &&
+      (L.size[MOE_REGION_XQ] >= lim || L.size[MOE_REGION_HQ] >= lim))
+    return fail(MOE_ERR_UNSUPPORTED, "staged activations (%zu bytes) and FC1 output (%zu bytes) must each be under 2 GiB",
+                L.size[MOE_REGION_XQ], L.size[MOE_REGION_HQ]);
+  return MOE_OK;
+}
+
 Layout compute_layout(const moe_config_t& cfg, const Tactic& t, int32_t max_rows, float capacity_factor) {
   Layout L;
   memset(&L, 0, sizeof(L));
@@ -167,6 +179,9 @@ extern "C" moe_status_t moe_workspace_query(const moe_config_t* cfg, int32_t exp
   if (s != MOE_OK) return s;
   if (!ws_bytes) return moe::fail(MOE_ERR_INVALID_ARG, "ws_bytes is NULL");
   moe::Tactic t = moe::choose_tactic(*cfg, expected_m);
-  *ws_bytes = moe::compute_layout(*cfg, t, max_rows, capacity_factor).total;
+  const moe::Layout L = moe::compute_layout(*cfg, t, max_rows, capacity_factor);
+  s = moe::validate_layout(*cfg, L);
+  if (s != MOE_OK) return s;
+  *ws_bytes = L.total;
   return MOE_OK;
 }

@@ -43,6 +43,8 @@ struct Layout {
 
 // Host-only logic (moe_host.cpp, no HIP dependency).
 int32_t token_bucket(int32_t tokens);
+// Limits that depend on the layout (call after compute_layout).
+moe_status_t validate_layout(const moe_config_t& cfg, const Layout& L);
 moe_status_t validate_config(const moe_config_t* cfg, int32_t expected_m, int32_t max_rows,
                              float capacity_factor);
 Tactic choose_tactic(const moe_config_t& cfg, int32_t expected_m);

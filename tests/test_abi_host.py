@@ -83,6 +83,28 @@ def test_query_rejects_bad_sizes(expected_m, max_rows, cf, status):
     assert ei.value.status == status
 
 
+def test_query_rejects_fp8_operands_of_2gib():
+    """The FP8 GEMMs gather token rows with 31-bit byte offsets: the FC1
+    output (route rows held * I bytes) and the staged activations must each
+    stay under 2 GiB."""
+    cfg = _cfg()
+    K, I = 8, 2048
+    rows = (1 << 31) // (K * I) - 1  # largest max_rows whose route rows * I < 2^31
+    L.moe_workspace_query(cfg, 64, rows, 1.0)
+    with pytest.raises(L.MoEError) as ei:
+        L.moe_workspace_query(cfg, 64, rows + 1, 1.0)
+    assert ei.value.status == L.MOE_ERR_UNSUPPORTED
+    # a capacity factor below one holds fewer route rows
+    L.moe_workspace_query(cfg, 64, rows + 1, 0.5)
+    # per-route staging keeps K activation rows per token
+    staged = _cfg(flags=L.MOE_FLAG_CHECK_ROUTES | L.MOE_FLAG_PER_ROUTE_STAGING)
+    x_rows = (1 << 31) // (K * 7168)
+    L.moe_workspace_query(staged, 64, x_rows - 1, 0.25)
+    with pytest.raises(L.MoEError) as ei:
+        L.moe_workspace_query(staged, 64, x_rows + 1, 0.25)
+    assert ei.value.status == L.MOE_ERR_UNSUPPORTED
+
+
 def test_query_sizes_scale_with_capacity_not_tactic():
     cfg = _cfg()
     a = L.moe_workspace_query(cfg, 8, 4096, 1.0)

@@ -227,6 +227,38 @@ def test_skewed_zipf_sampled():
     _sampled_full_size(CONFIGS["skewed"], 0, 24, "zipf T=8192")
 
 
+@pytest.mark.slow
+def test_dsv3_decode_sampled():
+    """The DSV3-like shape at decode token counts, each in the launch
+    configuration the benchmark uses for it: 16- and 32-token tiles, where
+    every workgroup streams three or four FC2 tiles back to back (each tile's
+    output stores still in flight while the next tile's first stages are
+    awaited).  A token's output depends only on its own routes, so one
+    oracle call over tokens sampled from the first 8, 64 and 100 serves all
+    three layers."""
+    base = CONFIGS["dsv3"]
+    shape = MoEShape(100, base.hidden, base.intermediate, base.experts, base.top_k, base.routing)
+    inp = make_layer_inputs(shape, seed=5)
+    dev = to_device(inp)
+    rng = np.random.default_rng(5)
+    tok = np.concatenate([np.arange(8), np.sort(rng.choice(np.arange(8, 64), 12, replace=False)),
+                          np.sort(rng.choice(np.arange(64, 100), 8, replace=False))])
+    res = M.forward_fp8(inp.x_bf16, inp.topk_idx, inp.topk_w, inp.w13, inp.w13_scale, inp.w2, inp.w2_scale,
+                        token_ids=tok)
+    for T, block_m in [(8, 16), (64, 16), (100, 32)]:
+        sub = MoEShape(T, base.hidden, base.intermediate, base.experts, base.top_k, base.routing)
+        layer = make_layer(sub, dev)
+        assert layer.tactic()["block_m"] == block_m
+        out = run_forward(layer, dev, tokens=T)
+        torch.cuda.synchronize()
+        assert layer.status() == 0
+        sel = tok < T
+        assert_output_close(_bits(out)[tok[sel]], res.out_bits[sel], f"dsv3 T={T}")
+        if T == shape.tokens:
+            _check_compaction(layer, res, shape, T)
+        del layer, out
+
+
 def _retile(w, fc1, inter):
     """NumPy statement of the 16x16x128 weight tile order (see moe_weights.hip)."""
     E, N, K = w.shape

@@ -3,8 +3,10 @@
 The named configurations exercise K in {2, 6, 8} and E in {8, 32}; here every
 supported top-k (1, 2, 4, 6, 8), expert counts from 1 to 1024, H and I from
 one to nine 128-column blocks (odd block counts leave the last FC2 column
-tile half full), token counts from 1 to 600 (all three compaction paths),
-masked routes and both weight formats are compared with the float64 oracle:
+tile half full), token counts from 1 to 600 (all three compaction paths), several FC2 tiles
+per workgroup (each tile's output stores still in flight while the next
+tile's first stages are awaited), masked routes and both weight formats are
+compared with the float64 oracle:
 the compaction bit for bit, the output within the layer tolerance.
 """
 
@@ -39,6 +41,11 @@ def _shapes():
         (300, 256, 128, 33, 8, 0.3, False),    # 2400 routes: compaction in its own launch
         (600, 128, 128, 9, 8, 0.0, False),     # 4800 routes: multi-workgroup compaction
         (600, 256, 256, 12, 8, 0.3, True),
+        # several FC2 tiles per workgroup, so a tile's first waits run while
+        # the previous tile's output stores are in flight
+        (128, 2048, 512, 256, 8, 0.3, False),  # 16-token tiles, 2048 FC2 tiles
+        (40, 4096, 1024, 64, 8, 0.0, False),   # 16-token tiles, 1024 FC2 tiles
+        (400, 4096, 384, 32, 8, 0.0, False),   # 128-token tiles, three-stage ring, 512 FC2 tiles
     ]
     return [(MoEShape(T, H, I, E, K, "topk"), m, mx, 100 + i) for i, (T, H, I, E, K, m, mx) in enumerate(table)]
 
