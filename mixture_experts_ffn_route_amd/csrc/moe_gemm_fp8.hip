@@ -43,6 +43,7 @@
 #include "moe_combine_dev.h"
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "moe_store_dev.h"
 
 namespace moe {
 
@@ -155,34 +156,6 @@ __device__ __forceinline__ void dma4o_scale(const void* base, uint32_t off, cons
 // launch, where FC2 tiles on other XCDs read them within the same kernel.
 __device__ __forceinline__ void store_wt_u32(uint8_t* p, uint32_t v) {
   __hip_atomic_store(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Raw buffer stores (gfx9 buffer resource: base, stride 0, num_records,
-// word 3 = 32-bit data format, no swizzle).  A store whose VGPR offset lies
-// past num_records is dropped by the hardware (the SGPR offset is not part
-// of that check, so it stays 0 here), so a store can be issued by every lane
-// with the masked lanes out of range.  Written as volatile asm so the
-// compiler neither merges nor removes any: the K loop's waits count them.
-constexpr uint32_t kBufferRsrcWord3 = 0x00020000u;
-// `base` and `num_records` are wave-uniform; readfirstlane says so, so the
-// descriptor sits in SGPRs as the instruction requires.
-__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t num_records) {
-  const uint64_t b = (uint64_t)(uintptr_t)base;
-  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b),
-               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xffffu),
-               (uint32_t)__builtin_amdgcn_readfirstlane(num_records), kBufferRsrcWord3};
-}
-// 8 bytes at base + voff + IMM (SGPR offset 0)
-template <int IMM>
-__device__ __forceinline__ void buffer_store8(u32x2 v, uint32_t voff, const u32x4& rsrc) {
-  static_assert(IMM >= 0 && IMM < 4096, "MUBUF offset field");
-  asm volatile("buffer_store_dwordx2 %0, %1, %2, 0 offen offset:%3"
-               :: "v"(v), "v"(voff), "s"(rsrc), "n"(IMM) : "memory");
-}
-// A store that writes nothing (an empty buffer): it only counts as an
-// outstanding vector-memory operation.
-__device__ __forceinline__ void buffer_store_none(const u32x4& empty_rsrc) {
-  asm volatile("buffer_store_dword %0, off, %1, 0" :: "v"(0u), "s"(empty_rsrc) : "memory");
 }
 
 // Polls of a readiness counter before a persistent FC2 tile gives up (each

@@ -29,6 +29,7 @@
 #include "moe_combine_dev.h"
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "moe_store_dev.h"
 
 namespace moe {
 namespace {
@@ -114,7 +115,6 @@ struct MxCfg {
   static constexpr int N_LD = 4 + 1 + B_INSTR + 1;
   static_assert(TBW >= 1 && NBH >= 1 && NBH <= 4 && STAGES >= 2, "tile shape");
   static_assert(BS_LANES <= 64 && (STAGES - 2) * N_LD < 64, "load shape");
-  static_assert(2 * 8 * BT * 4 <= STAGE, "epilogue scratch fits in ring stage 0");
 };
 
 template <int BT, bool FC1, int FA>
@@ -124,6 +124,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring1[C::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t ring2[C::STAGES > 2 ? C::STAGE : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t ring3[C::STAGES > 3 ? C::STAGE : 16];
+  // FC1 epilogue: per-32-row block maxima of h (pass 1) and of h - hi (pass
+  // 2), [16-row block][token]; outside the ring, which holds the next
+  // tile's first stages by then
+  __shared__ __attribute__((aligned(16))) float red_s[FC1 ? 2 * 8 * BT : 4];
   __shared__ int32_t cb_list[FC1 ? 1 : BT];  // FC2 fused combine: tokens this tile completes
   __shared__ int32_t cb_count;
   auto ring = [&](auto stage) -> lds_u8* {
@@ -154,32 +158,34 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
   const int sa_grp = (wn * C::NBH) / 4;
   const int sa_shift = 8 * ((wn * C::NBH) % 4);
 
-  if constexpr (!FC1) {
-    if (a.fc.out) zero_unrouted_rows(a.fc, (int)a.hdr[kHdrTokens], a.top_k, a.n_rows);
-  }
-  for (int64_t v = v_begin + slot; v < v_end; v += per_xcd) {
+  // ---- tile state, set one tile ahead: the next tile's first stages are
+  // issued before the current tile's epilogue, which hides their latency ----
+  int e = 0, p0 = 0, rows_valid = 1, nt = 0;
+  const uint8_t* a_src = a.w;
+  const uint32_t* as_src = a.w_scale;
+  const uint8_t* b_src[C::B_INSTR];
+  const uint32_t* bs_src = a.a_scale;
+  auto src_row = [&](int t) -> int64_t {
+    const int p = p0 + min(t, rows_valid - 1);
+    if (!FC1) return p;
+    const int r = a.sorted_route[p];
+    return r / a.top_k;
+  };
+  auto setup = [&](int64_t v) {
     const int64_t group = v / ((int64_t)kGroupM * a.n_tiles);
     const int64_t rem = v - group * kGroupM * a.n_tiles;
     const int m0 = (int)(group * kGroupM);
     const int gm = min(kGroupM, total_m - m0);
-    const int nt = (int)(rem / gm);
+    nt = (int)(rem / gm);
     const int mt = m0 + (int)(rem % gm);
-    const int e = __builtin_amdgcn_readfirstlane(a.tiles[2 * mt]);
-    const int p0 = __builtin_amdgcn_readfirstlane(a.tiles[2 * mt + 1]);
-    const int rows_valid = min(BT, __builtin_amdgcn_readfirstlane(a.offsets[e + 1]) - p0);
-
+    e = __builtin_amdgcn_readfirstlane(a.tiles[2 * mt]);
+    p0 = __builtin_amdgcn_readfirstlane(a.tiles[2 * mt + 1]);
+    rows_valid = min(BT, __builtin_amdgcn_readfirstlane(a.offsets[e + 1]) - p0);
     const int64_t tile0 = ((int64_t)e * a.n_tiles + nt) * kbs;
-    const uint8_t* a_src = a.w + tile0 * C::A_BYTES + (wave * 4 * 64 + lane) * 16;
-    const uint32_t* as_src = a.w_scale + tile0 * 256 + wave * 32 + (lane < 32 ? lane : 0);
-    auto src_row = [&](int t) -> int64_t {
-      const int p = p0 + min(t, rows_valid - 1);
-      if (!FC1) return p;
-      const int r = a.sorted_route[p];
-      return r / a.top_k;
-    };
+    a_src = a.w + tile0 * C::A_BYTES + (wave * 4 * 64 + lane) * 16;
+    as_src = a.w_scale + tile0 * 256 + wave * 32 + (lane < 32 ? lane : 0);
     // activation terms: piece V of the wave covers LDS chunk V/64 = (token
     // block, term, half); lane piece lp = (column group, token)
-    const uint8_t* b_src[C::B_INSTR];
 #pragma unroll
     for (int j = 0; j < C::B_INSTR; ++j) {
       const int pv = wave * C::B_PIECES + j * 64 + (lane < C::B_LANES ? lane : 0);
@@ -190,27 +196,54 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
     }
     // activation exponents: word U covers token block U/64, lane U%64 =
     // token (U%16) and 32-block (U%64)/16
-    const uint32_t* bs_src;
-    {
-      const int u = wave * C::BS_LANES + (lane < C::BS_LANES ? lane : 0);
-      const int lp = u & 63;
-      bs_src = a.a_scale + src_row((u >> 6) * 16 + (lp & 15)) * kq + (lp >> 4);
+    const int u = wave * C::BS_LANES + (lane < C::BS_LANES ? lane : 0);
+    const int lp = u & 63;
+    bs_src = a.a_scale + src_row((u >> 6) * 16 + (lp & 15)) * kq + (lp >> 4);
+  };
+
+  auto issue = [&](auto stage, int kb) {
+    const lds_u8* As = ring(stage);
+    const lds_u8* ASs = As + C::A_BYTES;
+    const lds_u8* Bs = ASs + C::AS_BYTES;
+    const lds_u8* BSs = Bs + C::B_BYTES;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(a_src + (int64_t)kb * C::A_BYTES + j * 1024, As + (wave * 4 + j) * 1024);
+    if (lane < 32) dma4(as_src + kb * 256, ASs + wave * 128);
+#pragma unroll
+    for (int j = 0; j < C::B_INSTR; ++j)
+      if (lane < C::B_LANES) dma16(b_src[j] + kb * kKB, Bs + (wave * C::B_PIECES + j * 64) * 16);
+    if (lane < C::BS_LANES) dma4(bs_src + kb * 4, BSs + wave * C::BS_LANES * 4);
+  };
+  auto prologue = [&]() {
+    issue(std::integral_constant<int, 0>{}, 0);
+    if (C::STAGES > 2 && 1 < kbs) issue(std::integral_constant<int, 1>{}, 1);
+    if (C::STAGES > 3 && 2 < kbs) issue(std::integral_constant<int, (C::STAGES > 3 ? 2 : 0)>{}, 2);
+  };
+
+  // FC2's output stores stay in flight into the next tile's first steps, as
+  // in the FP8 kernel: EPI_STORES buffer stores per wave, issued after the
+  // next tile's first STAGES - 1 stages, so the waits for those stages allow
+  // for EPI_STORES newer operations.  The first tile adds EPI_STORES stores
+  // that write nothing; the fused-combine epilogue waits for every
+  // outstanding operation before it stores.
+  constexpr bool kStoreOverlap = !FC1;
+  constexpr int kEpiStores = C::NB * C::TBW;
+  static_assert((C::STAGES - 2) * C::N_LD + kEpiStores < 64, "vmcnt range");
+
+  if constexpr (!FC1) {
+    if (a.fc.out) zero_unrouted_rows(a.fc, (int)a.hdr[kHdrTokens], a.top_k, a.n_rows);
+  }
+  int64_t v = v_begin + slot;
+  if (v < v_end) {
+    setup(v);
+    prologue();
+    if constexpr (kStoreOverlap) {
+      const st_u32x4 none = buffer_rsrc(a.y, 0u);
+#pragma unroll
+      for (int i = 0; i < kEpiStores; ++i) buffer_store_none(none);
     }
-
-    auto issue = [&](auto stage, int kb) {
-      const lds_u8* As = ring(stage);
-      const lds_u8* ASs = As + C::A_BYTES;
-      const lds_u8* Bs = ASs + C::AS_BYTES;
-      const lds_u8* BSs = Bs + C::B_BYTES;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dma16(a_src + (int64_t)kb * C::A_BYTES + j * 1024, As + (wave * 4 + j) * 1024);
-      if (lane < 32) dma4(as_src + kb * 256, ASs + wave * 128);
-#pragma unroll
-      for (int j = 0; j < C::B_INSTR; ++j)
-        if (lane < C::B_LANES) dma16(b_src[j] + kb * kKB, Bs + (wave * C::B_PIECES + j * 64) * 16);
-      if (lane < C::BS_LANES) dma4(bs_src + kb * 4, BSs + wave * C::BS_LANES * 4);
-    };
-
+  }
+  for (; v < v_end; v += per_xcd) {
     v4f acc[C::NB][C::TBW];
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb)
@@ -220,9 +253,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
     auto step = [&](auto stage, int kb) {
       constexpr int ST = decltype(stage)::value;
       const int ahead = min(C::STAGES - 2, kbs - 1 - kb);
-      if (C::STAGES >= 4 && ahead >= 2) wait_vmcnt<(C::STAGES >= 4 ? 2 : 0) * C::N_LD>();
-      else if (C::STAGES >= 3 && ahead >= 1) wait_vmcnt<(C::STAGES >= 3 ? 1 : 0) * C::N_LD>();
-      else wait_vmcnt<0>();
+      if (kStoreOverlap && ST <= C::STAGES - 2 && kb <= C::STAGES - 2) {
+        // stage kb came from the prologue, before the previous epilogue's stores
+        if (C::STAGES >= 4 && ahead >= 2) wait_vmcnt<(C::STAGES >= 4 ? 2 : 0) * C::N_LD + kEpiStores>();
+        else if (C::STAGES >= 3 && ahead >= 1) wait_vmcnt<(C::STAGES >= 3 ? 1 : 0) * C::N_LD + kEpiStores>();
+        else wait_vmcnt<kEpiStores>();
+      } else {
+        if (C::STAGES >= 4 && ahead >= 2) wait_vmcnt<(C::STAGES >= 4 ? 2 : 0) * C::N_LD>();
+        else if (C::STAGES >= 3 && ahead >= 1) wait_vmcnt<(C::STAGES >= 3 ? 1 : 0) * C::N_LD>();
+        else wait_vmcnt<0>();
+      }
       barrier_nofence();
       if (kb + C::STAGES - 1 < kbs)
         issue(std::integral_constant<int, (ST + C::STAGES - 1) % C::STAGES>{}, kb + C::STAGES - 1);
@@ -258,24 +298,34 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         aq = an;
       });
+      // every LDS read of this stage is complete before the next barrier
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     };
-    issue(std::integral_constant<int, 0>{}, 0);
-    if (C::STAGES > 2 && 1 < kbs) issue(std::integral_constant<int, 1>{}, 1);
-    if (C::STAGES > 3 && 2 < kbs) issue(std::integral_constant<int, (C::STAGES > 3 ? 2 : 0)>{}, 2);
     for (int kb = 0; kb < kbs; kb += C::STAGES) {
       step(std::integral_constant<int, 0>{}, kb);
       if (kb + 1 < kbs) step(std::integral_constant<int, 1>{}, kb + 1);
       if (C::STAGES > 2 && kb + 2 < kbs) step(std::integral_constant<int, (C::STAGES > 2 ? 2 : 0)>{}, kb + 2);
       if (C::STAGES > 3 && kb + 3 < kbs) step(std::integral_constant<int, (C::STAGES > 3 ? 3 : 0)>{}, kb + 3);
     }
-    __syncthreads();  // every wave is done with the ring before the epilogue reuses LDS
+    // Every wave is done reading the ring before the next tile's first
+    // stages go into it.  LDS-only barrier: nothing of this tile is in
+    // flight, and a fenced one would also wait for the previous tile's
+    // output stores.
+    barrier_nofence();
+    const int ep_p0 = p0, ep_rows = rows_valid, ep_nt = nt;
+    if (v + per_xcd < v_end) {
+      setup(v + per_xcd);
+      prologue();
+    }
 
     if (FC1) {
       // h = bf16(silu(g) * up), then the two-term split per 32 rows of h.
       // A lane holds 4 consecutive rows of a 16-row block for one token; a
       // 32-block is two row blocks, which may sit in different waves, so the
       // block maxima go through LDS: red[rb][t] (pass 1: |h|, pass 2: |h - hi|).
-      float* red1 = reinterpret_cast<float*>(ring0);
+      // The exchanges wait on LDS only: a fenced barrier would also wait for
+      // the next tile's stages issued above.
+      float* red1 = red_s;
       float* red2 = red1 + 8 * BT;
       const int iq = a.inter / 32;
       float hv[C::TBW][C::NBH][4];
@@ -295,7 +345,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
           m = fmaxf(m, __shfl_xor(m, 32));
           if (lane < 16) red1[(wn * C::NBH + g) * BT + wt * C::TW + tb * 16 + lane] = m;
         }
-      __syncthreads();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      barrier_nofence();
       uint32_t hi_codes[C::TBW][C::NBH];
       int ehi[C::TBW][C::NBH];
 #pragma unroll
@@ -318,7 +369,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
           m = fmaxf(m, __shfl_xor(m, 32));
           if (lane < 16) red2[rb * BT + t] = m;
         }
-      __syncthreads();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      barrier_nofence();
 #pragma unroll
       for (int tb = 0; tb < C::TBW; ++tb)
 #pragma unroll
@@ -329,41 +381,65 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
           const int elo = mx_block_exp(fmaxf(red2[r0 * BT + t], red2[(r0 + 1) * BT + t]));
           float unused[4];
           const uint32_t lo_codes = mx_term4(hv[tb][g], elo, unused);
-          if (t < rows_valid) {
-            const int64_t off = (int64_t)(p0 + t) * a.inter + nt * 128 + rb * 16 + 4 * (lane >> 4);
+          if (t < ep_rows) {
+            const int64_t off = (int64_t)(ep_p0 + t) * a.inter + ep_nt * 128 + rb * 16 + 4 * (lane >> 4);
             *reinterpret_cast<uint32_t*>(a.hq + off) = hi_codes[tb][g];
             *reinterpret_cast<uint32_t*>(a.hq + a.h_plane + off) = lo_codes;
             if ((rb & 1) == 0 && (lane >> 4) == 0)
-              a.hs[(int64_t)(p0 + t) * iq + nt * 4 + rb / 2] =
+              a.hs[(int64_t)(ep_p0 + t) * iq + ep_nt * 4 + rb / 2] =
                   (uint32_t)(ehi[tb][g] + 127) | ((uint32_t)(elo + 127) << 8);
           }
         }
     } else {
-      const int n0 = nt * kBN;
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) {
-        const int n = (nb < C::NBH ? wn * C::G + nb * 16 : 128 + wn * C::G + (nb - C::NBH) * 16) + 4 * (lane >> 4);
+      const int n0 = ep_nt * kBN;
+      if (a.fc.out == nullptr) {
+        // One buffer per 16-token block, from the block's first row, holding
+        // only its valid rows: a lane's row and column are in the VGPR offset
+        // (bounds-checked), the weight block in the instruction offset.  Rows
+        // past ep_rows fall past the buffer's end; the second 128-row weight
+        // block, when it lies past H, stores into an empty buffer.
+        const uint32_t v_lane = (uint32_t)(((lane & 15) * a.n_rows + n0 + wn * C::G + 4 * (lane >> 4)) * 2);
+        const bool hi_ok = n0 + 128 < a.n_rows;
+        const st_u32x4 empty = buffer_rsrc(a.y, 0u);
 #pragma unroll
         for (int tb = 0; tb < C::TBW; ++tb) {
-          const int t = wt * C::TW + tb * 16 + (lane & 15);
-          if (t < rows_valid && n0 + n < a.n_rows) {
+          const int r0 = wt * C::TW + tb * 16;
+          const int rows = min(max(ep_rows - r0, 0), 16);
+          const st_u32x4 rs = buffer_rsrc(a.y + (int64_t)(ep_p0 + r0) * a.n_rows, (uint32_t)(rows * a.n_rows * 2));
+          const st_u32x4 rs_hi = hi_ok ? rs : empty;
+          static_for<0, C::NB>([&](auto nbc) {
+            constexpr int nb = decltype(nbc)::value;
             u32x2 o;
             o[0] = bf16x2_rne(acc[nb][tb][0], acc[nb][tb][1]);
             o[1] = bf16x2_rne(acc[nb][tb][2], acc[nb][tb][3]);
-            uint16_t* dst = a.y + (int64_t)(p0 + t) * a.n_rows + n0 + n;
-            if (a.fc.out)
-              store_y_coherent(dst, o[0], o[1]);  // read by the workgroup that completes the token
+            if constexpr (nb < C::NBH)
+              buffer_store8<nb * 16 * 2>(o, v_lane, rs);
             else
-              *reinterpret_cast<u32x2*>(dst) = o;
+              buffer_store8<(128 + (nb - C::NBH) * 16) * 2>(o, v_lane, rs_hi);
+          });
+        }
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) {
+          const int n = (nb < C::NBH ? wn * C::G + nb * 16 : 128 + wn * C::G + (nb - C::NBH) * 16) + 4 * (lane >> 4);
+#pragma unroll
+          for (int tb = 0; tb < C::TBW; ++tb) {
+            const int t = wt * C::TW + tb * 16 + (lane & 15);
+            if (t < ep_rows && n0 + n < a.n_rows) {
+              u32x2 o;
+              o[0] = bf16x2_rne(acc[nb][tb][0], acc[nb][tb][1]);
+              o[1] = bf16x2_rne(acc[nb][tb][2], acc[nb][tb][3]);
+              store_y_coherent(a.y + (int64_t)(ep_p0 + t) * a.n_rows + n0 + n, o[0], o[1]);  // read by the workgroup that completes the token
+            }
           }
         }
-      }
-      if (a.fc.out)
-        arrive_and_combine<kThreads>(a.fc, a.y, a.sorted_route, a.top_k, a.n_rows, a.n_tiles, p0, rows_valid, nt,
+        // (its opening vmcnt(0) also completes the next tile's prologue
+        // stages, so the next tile's first waits hold without more stores)
+        arrive_and_combine<kThreads>(a.fc, a.y, a.sorted_route, a.top_k, a.n_rows, a.n_tiles, ep_p0, ep_rows, ep_nt,
                                      (__attribute__((address_space(3))) int32_t*)cb_list,
                                      (__attribute__((address_space(3))) int32_t*)&cb_count);
+      }
     }
-    __syncthreads();  // the next tile's DMA reuses the LDS the epilogue read
   }
 }
 
