@@ -150,6 +150,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
   const int slot = blockIdx.x >> 3;
   const int per_xcd = gridDim.x >> 3;
   const int64_t v_begin = total * xcd / 8, v_end = total * (xcd + 1) / 8;
+  // Active slots of this XCD: the fewest that still finish its tiles in
+  // ceil(tiles / slots) rounds, so that every active workgroup streams in
+  // every round (with 112 tiles on 32 slots: 28 slots x 4 rounds rather
+  // than 16 x 4 + 16 x 3, whose last round runs half the XCD's CUs).
+  const int64_t rounds = (v_end - v_begin + per_xcd - 1) / per_xcd;
+  const int stride = rounds > 0 ? (int)((v_end - v_begin + rounds - 1) / rounds) : per_xcd;
   const uint32_t a_lane = (uint32_t)(wn * C::NBH) * 2048u + (uint32_t)lane * 16u;
   const uint32_t b_lane = (uint32_t)(wt * C::TBW) * 4096u + (uint32_t)lane * 16u;
   const uint32_t bs_lane = (uint32_t)(wt * C::TBW * 64 + lane);
@@ -233,7 +239,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
   if constexpr (!FC1) {
     if (a.fc.out) zero_unrouted_rows(a.fc, (int)a.hdr[kHdrTokens], a.top_k, a.n_rows);
   }
-  int64_t v = v_begin + slot;
+  int64_t v = slot < stride ? v_begin + slot : v_end;
   if (v < v_end) {
     setup(v);
     prologue();
@@ -243,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
       for (int i = 0; i < kEpiStores; ++i) buffer_store_none(none);
     }
   }
-  for (; v < v_end; v += per_xcd) {
+  for (; v < v_end; v += stride) {
     v4f acc[C::NB][C::TBW];
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb)
@@ -313,8 +319,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
     // output stores.
     barrier_nofence();
     const int ep_p0 = p0, ep_rows = rows_valid, ep_nt = nt;
-    if (v + per_xcd < v_end) {
-      setup(v + per_xcd);
+    if (v + stride < v_end) {
+      setup(v + stride);
       prologue();
     }
 
