@@ -135,6 +135,14 @@ __device__ __forceinline__ void dma16o(const void* base, uint32_t off, const lds
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(off), "s"(base), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
 }
+// The weight stream of a tile that no other workgroup reads: non-temporal,
+// so the lines do not displace reused data on their way through the
+// caches (measured at T=8: W13 streams at 6.6 TB/s against 5.9 with the
+// default policy).
+__device__ __forceinline__ void dma16o_nt(const void* base, uint32_t off, const lds_u8* lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :: "v"(off), "s"(base), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
+}
 __device__ __forceinline__ void dma4o(const void* base, uint32_t off, const lds_u8* lds_wave_base) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
                :: "v"(off), "s"(base), "s"(lds_addr(lds_wave_base)) : "memory", "m0");

@@ -74,6 +74,12 @@ __device__ __forceinline__ void dma16(const uint8_t* src, const lds_u8* lds_wave
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(src), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
 }
+// Weights of a tile that no other workgroup reads stream non-temporally
+// (see the FP8 kernel).
+__device__ __forceinline__ void dma16_nt(const uint8_t* src, const lds_u8* lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :: "v"(src), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
+}
 __device__ __forceinline__ void dma4(const uint32_t* src, const lds_u8* lds_wave_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                :: "v"(src), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
@@ -167,6 +173,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
   // ---- tile state, set one tile ahead: the next tile's first stages are
   // issued before the current tile's epilogue, which hides their latency ----
   int e = 0, p0 = 0, rows_valid = 1, nt = 0;
+  bool w_once = false;  // the tile's expert has a single row tile: no other workgroup reads its weights
   const uint8_t* a_src = a.w;
   const uint32_t* as_src = a.w_scale;
   const uint8_t* b_src[C::B_INSTR];
@@ -187,6 +194,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
     e = __builtin_amdgcn_readfirstlane(a.tiles[2 * mt]);
     p0 = __builtin_amdgcn_readfirstlane(a.tiles[2 * mt + 1]);
     rows_valid = min(BT, __builtin_amdgcn_readfirstlane(a.offsets[e + 1]) - p0);
+    w_once = __builtin_amdgcn_readfirstlane(a.offsets[e + 1]) - __builtin_amdgcn_readfirstlane(a.offsets[e]) <= BT;
     const int64_t tile0 = ((int64_t)e * a.n_tiles + nt) * kbs;
     a_src = a.w + tile0 * C::A_BYTES + (wave * 4 * 64 + lane) * 16;
     as_src = a.w_scale + tile0 * 256 + wave * 32 + (lane < 32 ? lane : 0);
@@ -212,8 +220,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
     const lds_u8* ASs = As + C::A_BYTES;
     const lds_u8* Bs = ASs + C::AS_BYTES;
     const lds_u8* BSs = Bs + C::B_BYTES;
+    if (w_once) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(a_src + (int64_t)kb * C::A_BYTES + j * 1024, As + (wave * 4 + j) * 1024);
+      for (int j = 0; j < 4; ++j) dma16_nt(a_src + (int64_t)kb * C::A_BYTES + j * 1024, As + (wave * 4 + j) * 1024);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma16(a_src + (int64_t)kb * C::A_BYTES + j * 1024, As + (wave * 4 + j) * 1024);
+    }
     if (lane < 32) dma4(as_src + kb * 256, ASs + wave * 128);
 #pragma unroll
     for (int j = 0; j < C::B_INSTR; ++j)
