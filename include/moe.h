@@ -181,7 +181,7 @@ enum {
   MOE_REGION_HQ = 9,            /* FC1 output rows: e4m3 [row_cap, I]; MXFP8: [2][row_cap, I] hi/lo-term codes */
   MOE_REGION_HS = 10,           /* float32 [row_cap, I/128]; MXFP8: uint32 [row_cap, I/32] E8M0 pairs */
   MOE_REGION_Y = 11,            /* bf16 [row_cap, H] un-weighted FC2 rows */
-  MOE_REGION_TILES = 12,        /* int32 [max_m_tiles, 2] (expert, first sorted row) */
+  MOE_REGION_TILES = 12,        /* int32 [max_m_tiles, 4] (expert, first sorted row, rows, 1 if the expert's only tile) */
   MOE_REGION_W13T = 13,         /* e4m3 w13 tiled at create: [E, I/128, H/128] tiles of 32 KB */
   MOE_REGION_W2T = 14,          /* e4m3 w2 tiled at create: [E, ceil(H/256), I/128] tiles of 32 KB */
   MOE_REGION_W13S = 15,         /* MXFP8: w13 E8M0 tiled at create, 1 KB per w13 tile (empty for FP8) */

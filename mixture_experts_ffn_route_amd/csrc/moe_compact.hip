@@ -7,7 +7,7 @@
 //   offsets[e]       exclusive prefix of counts (E+1 entries)
 //   sorted_route[p]  route ids, expert-major, ascending r within an expert
 //   route_pos[r]     p such that sorted_route[p] == r, or -1
-//   tiles[m]         (expert, first sorted row) of each BLOCK_M row tile
+//   tiles[m]         (expert, first sorted row, rows, only-tile flag) of each BLOCK_M row tile
 // Routes whose expert-major position reaches the row capacity are dropped
 // and flagged (MOE_DEV_CAPACITY).
 //

@@ -150,8 +150,10 @@ __device__ inline void finish_counts(const CompactArgs& a, int* cnt, int* tmp, i
     const int kept_hi = (e + 1 < E) ? min(tmp[e + 1], cap) : min(total, cap);
     int m = cnt[e];
     for (int p = lo; p < kept_hi; p += a.block_m, ++m) {
-      a.tiles[2 * m] = e;
-      a.tiles[2 * m + 1] = p;
+      a.tiles[4 * m] = e;
+      a.tiles[4 * m + 1] = p;
+      a.tiles[4 * m + 2] = min(a.block_m, kept_hi - p);        // rows of this tile
+      a.tiles[4 * m + 3] = kept_hi - lo <= a.block_m ? 1 : 0;  // the expert's only row tile
       if (a.ready) a.ready[m] = 0;
     }
   }

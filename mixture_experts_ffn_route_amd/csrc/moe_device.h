@@ -6,6 +6,16 @@
 
 namespace moe {
 
+typedef int32_t tile_rec_t __attribute__((ext_vector_type(4)));
+
+// Row tile m of the compaction's tile list: (expert, first sorted row, rows,
+// 1 if it is the expert's only row tile).  Written by an earlier launch and
+// read through the scalar cache (one 16-byte load, counted on lgkmcnt); `m`
+// is wave-uniform.
+__device__ __forceinline__ tile_rec_t load_tile_rec(const int32_t* tiles, int m) {
+  return ((const __attribute__((address_space(4))) tile_rec_t*)tiles)[m];
+}
+
 constexpr float kE4m3Max = 448.0f;
 
 // bfloat16 bits -> float (exact).

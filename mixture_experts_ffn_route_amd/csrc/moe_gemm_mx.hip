@@ -184,17 +184,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
     const int r = a.sorted_route[p];
     return r / a.top_k;
   };
-  auto setup = [&](int64_t v) {
+  // Row tile of tile index v (token tiles grouped kGroupM deep, column tile
+  // fastest within a group).
+  auto row_tile = [&](int64_t v) -> int {
+    const int64_t group = v / ((int64_t)kGroupM * a.n_tiles);
+    const int64_t rem = v - group * kGroupM * a.n_tiles;
+    const int g0 = (int)(group * kGroupM);
+    return g0 + (int)(rem % min(kGroupM, total_m - g0));
+  };
+  // `rec` is the row tile's record (load_tile_rec), fetched ahead of time.
+  auto setup = [&](int64_t v, tile_rec_t rec) {
     const int64_t group = v / ((int64_t)kGroupM * a.n_tiles);
     const int64_t rem = v - group * kGroupM * a.n_tiles;
     const int m0 = (int)(group * kGroupM);
     const int gm = min(kGroupM, total_m - m0);
     nt = (int)(rem / gm);
-    const int mt = m0 + (int)(rem % gm);
-    e = __builtin_amdgcn_readfirstlane(a.tiles[2 * mt]);
-    p0 = __builtin_amdgcn_readfirstlane(a.tiles[2 * mt + 1]);
-    rows_valid = min(BT, __builtin_amdgcn_readfirstlane(a.offsets[e + 1]) - p0);
-    w_once = __builtin_amdgcn_readfirstlane(a.offsets[e + 1]) - __builtin_amdgcn_readfirstlane(a.offsets[e]) <= BT;
+    e = __builtin_amdgcn_readfirstlane(rec[0]);
+    p0 = __builtin_amdgcn_readfirstlane(rec[1]);
+    rows_valid = __builtin_amdgcn_readfirstlane(rec[2]);
+    w_once = __builtin_amdgcn_readfirstlane(rec[3]) != 0;
     const int64_t tile0 = ((int64_t)e * a.n_tiles + nt) * kbs;
     a_src = a.w + tile0 * C::A_BYTES + (wave * 4 * 64 + lane) * 16;
     as_src = a.w_scale + tile0 * 256 + wave * 32 + (lane < 32 ? lane : 0);
@@ -254,7 +262,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
   }
   int64_t v = slot < stride ? v_begin + slot : v_end;
   if (v < v_end) {
-    setup(v);
+    setup(v, load_tile_rec(a.tiles, row_tile(v)));
     prologue();
     if constexpr (kStoreOverlap) {
       const st_u32x4 none = buffer_rsrc(a.y, 0u);
@@ -263,6 +271,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
     }
   }
   for (; v < v_end; v += stride) {
+    // the next tile's record, in flight while this tile's first stage lands
+    tile_rec_t rec_next = {0, 0, 1, 0};
+    if (v + stride < v_end) rec_next = load_tile_rec(a.tiles, row_tile(v + stride));
     v4f acc[C::NB][C::TBW];
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb)
@@ -333,7 +344,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
     barrier_nofence();
     const int ep_p0 = p0, ep_rows = rows_valid, ep_nt = nt;
     if (v + stride < v_end) {
-      setup(v + stride);
+      setup(v + stride, rec_next);
       prologue();
     }
 

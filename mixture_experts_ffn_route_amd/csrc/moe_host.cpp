@@ -133,7 +133,7 @@ Layout compute_layout(const moe_config_t& cfg, const Tactic& t, int32_t max_rows
   L.size[MOE_REGION_HQ] = L.row_cap * I * (mx ? 2 : 1);
   L.size[MOE_REGION_HS] = mx ? L.row_cap * (I / 32) * 4 : L.row_cap * (I / 128) * 4;
   L.size[MOE_REGION_Y] = L.row_cap * H * 2;
-  L.size[MOE_REGION_TILES] = L.max_m_tiles * 2 * 4;
+  L.size[MOE_REGION_TILES] = L.max_m_tiles * 4 * 4;
   // create-time tiled copies of the e4m3 weights (FC2 padded to 256-row tiles)
   L.size[MOE_REGION_W13T] = E * (2 * I) * H;
   L.size[MOE_REGION_W2T] = E * ((H + 255) / 256 * 256) * I;

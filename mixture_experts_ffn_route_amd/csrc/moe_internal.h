@@ -87,7 +87,7 @@ struct CompactArgs {
   int32_t* offsets;        // [E+1]
   int32_t* sorted_route;   // [row_cap]
   int32_t* route_pos;      // [routes]
-  int32_t* tiles;          // [max_m_tiles, 2]
+  int32_t* tiles;          // [max_m_tiles, 4] (expert, first sorted row, rows, only-tile flag)
   int32_t* ready;          // [max_m_tiles] persistent FC1->FC2 counters, zeroed per listed tile (or null)
 };
 int launch_compact(const CompactArgs& a, void* stream);
@@ -117,7 +117,7 @@ struct GemmArgs {
   int32_t inter;           // I (FC1 gate/up split)
   int32_t n_tiles;         // output column tiles
   // tiles
-  const int32_t* tiles;    // (expert, first sorted row)
+  const int32_t* tiles;    // [m] = (expert, first sorted row, rows, 1 if the expert's only row tile)
   const int32_t* offsets;  // kept offsets [E+1]
   const uint32_t* hdr;
   // outputs
@@ -158,7 +158,7 @@ struct MxGemmArgs {
   const uint8_t* w;          // e4m3 weight tiles, MX operand order ([E, n_tiles, K/128] x 32 KB)
   const uint32_t* w_scale;   // E8M0 weight scale tiles ([E, n_tiles, K/128] x 256 words)
   int32_t n_rows, k_dim, inter, n_tiles;
-  const int32_t* tiles;
+  const int32_t* tiles;    // [m] = (expert, first sorted row, rows, 1 if the expert's only row tile)
   const int32_t* offsets;
   const uint32_t* hdr;
   uint8_t* hq;               // FC1: hi-term rows [R, I]; lo-term rows h_plane bytes further
