@@ -65,6 +65,7 @@ COUNTER_FILE = os.path.join(ROOT, "profiles", "fc1_dsv3_T4096_hbm_counters.txt")
 COUNTER_SOURCES = ["mixture_experts_ffn_route_amd/csrc/moe_gemm_fp8.hip",
                    "mixture_experts_ffn_route_amd/csrc/moe_gemm_fp8_body.inc",
                    "mixture_experts_ffn_route_amd/csrc/moe_device.h",
+                   "mixture_experts_ffn_route_amd/csrc/moe_store_dev.h",
                    "mixture_experts_ffn_route_amd/csrc/moe_host.cpp",
                    "mixture_experts_ffn_route_amd/csrc/moe_api.cpp"]
 

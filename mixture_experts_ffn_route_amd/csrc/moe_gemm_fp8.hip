@@ -202,7 +202,13 @@ struct Cfg {
   static constexpr int S_LANES = BT / kWaves;                     // scale loads per wave
   static constexpr int N_LD = A_INSTR + B_INSTR + 2;              // vector loads per wave per stage
   static_assert(TBW >= 1 && NB >= 2 && STAGES >= 2, "tile shape");
-  static constexpr int EPI_STORES = NB * TBW;                     // FC2 output stores per wave per tile
+  // FC2 output: the tile's BF16 rows go through a free ring stage (the last
+  // slot, which the next tile's prologue leaves empty), Y_ROWS rows per pass,
+  // and leave it as 16-byte stores of whole rows: BT / 16 per wave.
+  static constexpr int Y_PASSES = BT <= 64 ? 1 : 2;
+  static constexpr int Y_ROWS = BT / Y_PASSES;
+  static constexpr int EPI_STORES = BT / 16;                      // FC2 output stores per wave per tile
+  static_assert(Y_ROWS * 512 <= STAGE && Y_ROWS % 16 == 0 && TW % 16 == 0, "output staging");
   static_assert((STAGES - 2) * N_LD + EPI_STORES < 64, "vmcnt range");
 };
 

@@ -34,6 +34,15 @@ __device__ __forceinline__ void buffer_store8(st_u32x2 v, uint32_t voff, const s
                :: "v"(v), "v"(voff), "s"(rsrc), "n"(IMM) : "memory");
 }
 
+// 16 bytes at base + voff (SGPR offset 0).  A vector-memory store of more
+// than 64 bits reads its data VGPRs after issue: a VALU write to them within
+// the next two wait states (gfx940 and later) would be what gets stored.
+// The compiler inserts those wait states only after stores it emits itself,
+// not after inline asm, so the s_nop is part of the statement.
+__device__ __forceinline__ void buffer_store16(st_u32x4 v, uint32_t voff, const st_u32x4& rsrc) {
+  asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen\n\ts_nop 1" :: "v"(v), "v"(voff), "s"(rsrc) : "memory");
+}
+
 // A store that writes nothing (an empty buffer): it only counts as an
 // outstanding vector-memory operation.
 __device__ __forceinline__ void buffer_store_none(const st_u32x4& empty_rsrc) {
