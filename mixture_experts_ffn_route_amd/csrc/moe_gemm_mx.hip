@@ -248,13 +248,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
   };
 
   // FC2's output stores stay in flight into the next tile's first steps, as
-  // in the FP8 kernel: EPI_STORES buffer stores per wave, issued after the
+  // in the FP8 kernel: kEpiStores buffer stores per wave, issued after the
   // next tile's first STAGES - 1 stages, so the waits for those stages allow
-  // for EPI_STORES newer operations.  The first tile adds EPI_STORES stores
-  // that write nothing; the fused-combine epilogue waits for every
+  // for kEpiStores newer operations.  The tile's BF16 rows go out through
+  // the ring's last stage, whole rows per store (two 512-byte rows per
+  // instruction): BT / 16 stores per wave.  The first tile adds kEpiStores
+  // stores that write nothing; the fused-combine epilogue waits for every
   // outstanding operation before it stores.
   constexpr bool kStoreOverlap = !FC1;
-  constexpr int kEpiStores = C::NB * C::TBW;
+  constexpr int kEpiStores = BT / 16;
+  static_assert(BT * 512 <= C::STAGE, "output staging");
   static_assert((C::STAGES - 2) * C::N_LD + kEpiStores < 64, "vmcnt range");
 
   if constexpr (!FC1) {
@@ -423,30 +426,47 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
     } else {
       const int n0 = ep_nt * kBN;
       if (a.fc.out == nullptr) {
-        // One buffer per 16-token block, from the block's first row, holding
-        // only its valid rows: a lane's row and column are in the VGPR offset
-        // (bounds-checked), the weight block in the instruction offset.  Rows
-        // past ep_rows fall past the buffer's end; the second 128-row weight
-        // block, when it lies past H, stores into an empty buffer.
-        const uint32_t v_lane = (uint32_t)(((lane & 15) * a.n_rows + n0 + wn * C::G + 4 * (lane >> 4)) * 2);
+        // The tile's rows are transposed through the ring's last stage (free:
+        // the next tile's prologue fills the others): a lane's MFMA outputs
+        // are 4 columns of one row, so direct stores would write 32-byte
+        // pieces of 16 rows.  LDS holds BT rows x 32 chunks of 16 bytes,
+        // chunk c of row r at position c ^ (r & 31).  One buffer from the
+        // tile's first row holds only its valid rows, so rows past ep_rows
+        // fall past its end; with an odd number of 128-column blocks in H,
+        // the last tile's second half (chunks 16..31) goes out of range.
+        lds_u8* ys = ring(std::integral_constant<int, C::STAGES - 1>{});
         const bool hi_ok = n0 + 128 < a.n_rows;
-        const st_u32x4 empty = buffer_rsrc(a.y, 0u);
+        // an opaque copy of the lane index keeps the address terms from being
+        // hoisted out of the tile loop (and held across the K loop)
+        int ln;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+        const int lq4 = 4 * (ln >> 4), lr = ln & 15;
 #pragma unroll
         for (int tb = 0; tb < C::TBW; ++tb) {
-          const int r0 = wt * C::TW + tb * 16;
-          const int rows = min(max(ep_rows - r0, 0), 16);
-          const st_u32x4 rs = buffer_rsrc(a.y + (int64_t)(ep_p0 + r0) * a.n_rows, (uint32_t)(rows * a.n_rows * 2));
-          const st_u32x4 rs_hi = hi_ok ? rs : empty;
-          static_for<0, C::NB>([&](auto nbc) {
-            constexpr int nb = decltype(nbc)::value;
+          const int r = wt * C::TW + tb * 16 + lr;
+#pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb) {
+            // first of this lane's 4 columns
+            const int c = (nb < C::NBH ? wn * C::G + nb * 16 : 128 + wn * C::G + (nb - C::NBH) * 16) + lq4;
             u32x2 o;
             o[0] = bf16x2_rne(acc[nb][tb][0], acc[nb][tb][1]);
             o[1] = bf16x2_rne(acc[nb][tb][2], acc[nb][tb][3]);
-            if constexpr (nb < C::NBH)
-              buffer_store8<nb * 16 * 2>(o, v_lane, rs);
-            else
-              buffer_store8<(128 + (nb - C::NBH) * 16) * 2>(o, v_lane, rs_hi);
-          });
+            *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+                ys + r * 512 + (((c >> 3) ^ (r & 31)) << 4) + (c & 7) * 2) = o;
+          }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        barrier_nofence();
+        // whole rows out: wave w stores the row pairs w * BT / 16 ..
+        const int rd_row = ln >> 5, rd_chunk = ln & 31;
+        const uint32_t rd_col_off = (uint32_t)((n0 + rd_chunk * 8) * 2);
+        const st_u32x4 rs = buffer_rsrc(a.y + (int64_t)ep_p0 * a.n_rows, (uint32_t)(ep_rows * a.n_rows * 2));
+#pragma unroll
+        for (int i = 0; i < BT / 16; ++i) {
+          const int r = (wave * (BT / 16) + i) * 2 + rd_row;
+          const u32x4 d = *reinterpret_cast<lds_u32x4*>(ys + r * 512 + ((rd_chunk ^ (r & 31)) << 4));
+          const uint32_t voff = (rd_chunk < 16 || hi_ok) ? (uint32_t)(r * a.n_rows * 2) + rd_col_off : 0x7ffffff0u;
+          buffer_store16(d, voff, rs);
         }
       } else {
 #pragma unroll
