@@ -28,7 +28,7 @@ struct moe_layer {
   int32_t expected_m;
   float capacity_factor;
   int32_t staged_tokens;
-  bool compacted;  // the staging launch also compacted the routes (small batches)
+  bool compacted;  // the staging launch also scattered the routes (one compaction workgroup)
   void* out;
   int32_t grid_fc1, grid_fc2;
   int32_t grid_persist;  // MOE_FLAG_PERSISTENT_FFN: cooperative grid of the FC1->FC2 launch
@@ -81,9 +81,13 @@ moe::CompactArgs compact_args(moe_layer* l, int32_t T) {
   ca.num_experts = l->cfg.num_experts;
   ca.row_cap = (int32_t)l->L.row_cap;
   ca.block_m = l->tac.block_m;
-  ca.blocks = (routes + moe::kCompactChunk - 1) / moe::kCompactChunk;
+  ca.blocks = moe::compact_blocks_for(T, l->cfg.top_k);
+  ca.chunk = moe::compact_chunk_tokens(l->cfg.top_k) * l->cfg.top_k;
   ca.hdr = region<uint32_t>(l, MOE_REGION_STATUS);
+  // internal region: bases [compact_blocks, E], status [compact_blocks], arrival counter
   ca.blk_base = region<int32_t>(l, moe::kRegionBlkBase);
+  ca.blk_status = reinterpret_cast<uint32_t*>(ca.blk_base + l->L.compact_blocks * l->cfg.num_experts);
+  ca.arrive = ca.blk_base + l->L.compact_blocks * (l->cfg.num_experts + 1);
   ca.counts = region<int32_t>(l, MOE_REGION_COUNTS);
   ca.offsets = region<int32_t>(l, MOE_REGION_OFFSETS);
   ca.sorted_route = region<int32_t>(l, MOE_REGION_SORTED_ROUTE);
@@ -200,6 +204,10 @@ extern "C" moe_status_t moe_layer_create(const moe_config_t* cfg, int32_t expect
          moe::launch_tile_mx_scales(static_cast<const uint8_t*>(w->w2_scale),
                                     reinterpret_cast<uint32_t*>(l->ws + L.off[MOE_REGION_W2S]), E, H, I,
                                     (H + 255) / 256, I, false, stream) == 0;
+  // the compaction's arrival counter starts at zero (each staging leaves it so)
+  if (ok)
+    ok = moe::launch_fill_zero(reinterpret_cast<uint32_t*>(l->ws + L.off[moe::kRegionBlkBase]),
+                               (int64_t)(L.size[moe::kRegionBlkBase] / 4), stream) == 0;
   // arrival counters of the fused combine start at zero (each forward leaves them so)
   if (ok && (cfg->flags & MOE_FLAG_FUSED_COMBINE))
     ok = moe::launch_fill_zero(reinterpret_cast<uint32_t*>(l->ws + L.off[MOE_REGION_ARRIVE]),
@@ -253,15 +261,13 @@ extern "C" moe_status_t moe_stage_inputs(moe_layer_t* l, const void* x, const fl
   a.xs = region<float>(l, MOE_REGION_XS);
   a.x_plane = (int64_t)l->L.rows_x * l->cfg.hidden;
   a.xs_mx = region<uint32_t>(l, MOE_REGION_XS);
-  // Small batches (up to kFuseRoutes routes) stage and compact in one launch;
-  // the compaction is then one workgroup, which beyond that size costs more
-  // than the separate launches it saves.  Larger ones compact in the forward.
-  const bool fuse = (int64_t)num_tokens * l->cfg.top_k <= moe::kFuseRoutes;
+  // One launch stages and compacts; a compaction over several workgroups
+  // leaves its scatter to the forward.
+  const moe::CompactArgs ca = compact_args(l, num_tokens);
   const int p = prof_begin(l, MOE_KERNEL_STAGE, s);
-  const int rc = fuse ? moe::launch_stage_compact(a, compact_args(l, num_tokens), stream) : moe::launch_stage(a, stream);
-  if (rc != 0) return hip_fail("stage launch");
+  if (moe::launch_stage(a, ca, stream) != 0) return hip_fail("stage launch");
   prof_end(l, p, s);
-  l->compacted = fuse;
+  l->compacted = ca.blocks == 1;
   l->staged_tokens = num_tokens;
   l->out = out_bf16;
   return MOE_OK;
@@ -279,7 +285,7 @@ extern "C" moe_status_t moe_layer_forward(moe_layer_t* l, void* stream) {
   int p = -1;
   if (!l->compacted) {
     p = prof_begin(l, MOE_KERNEL_COMPACT, s);
-    if (moe::launch_compact(ca, stream) != 0) return hip_fail("compact launch");
+    if (moe::launch_compact_scatter(ca, stream) != 0) return hip_fail("compact launch");
     prof_end(l, p, s);
   }
 

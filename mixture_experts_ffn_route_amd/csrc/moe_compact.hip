@@ -14,7 +14,9 @@
 // Ranking is stable and deterministic: within a wavefront, lanes holding the
 // same expert find each other with one ballot per expert-id bit, and a lane's
 // rank is the popcount of its peers below it; waves walk contiguous route
-// ranges in order and keep running per-expert counts in LDS.
+// ranges in order and keep running per-expert counts in LDS.  Workgroups
+// take whole tokens, at most kCompactChunk routes each; the counting runs in
+// the staging launch (moe_stage.hip), beside the activation quantisation.
 #include <hip/hip_runtime.h>
 
 #include "moe_compact_dev.h"
@@ -23,53 +25,9 @@
 
 namespace moe {
 
-// Single-workgroup path (routes <= kCompactChunk): count, scan, scatter.
-__global__ __launch_bounds__(kCompactThreads) void compact_fused_kernel(CompactArgs a) {
-  extern __shared__ int lds[];
-  compact_one_workgroup(a, lds);
-}
-
-// Multi-workgroup path, kernel 1: per-block per-expert counts -> blk_base.
-__global__ __launch_bounds__(kCompactThreads) void compact_count_kernel(CompactArgs a) {
-  extern __shared__ int lds[];
-  const int E = a.num_experts;
-  int* hist = lds;
-  int rank[kItems], expert[kItems];
-  clear_hist(hist, kCompactWaves * E);
-  __syncthreads();
-  sweep(a, blockIdx.x, hist, rank, expert);
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kCompactThreads) {
-    int s = 0;
-    for (int w = 0; w < kCompactWaves; ++w) s += hist[w * E + e];
-    a.blk_base[(int64_t)blockIdx.x * E + e] = s;
-  }
-}
-
-// Kernel 2 (one workgroup): per-expert totals, offsets, per-block bases, tiles.
-__global__ __launch_bounds__(kCompactThreads) void compact_scan_kernel(CompactArgs a) {
-  extern __shared__ int lds[];
-  const int E = a.num_experts;
-  int* cnt = lds;
-  int* tmp = cnt + E;
-  int* scalar = tmp + E + 1;
-  for (int e = threadIdx.x; e < E; e += kCompactThreads) {
-    int run = 0;
-    for (int b = 0; b < a.blocks; ++b) {
-      const int c = a.blk_base[(int64_t)b * E + e];
-      a.blk_base[(int64_t)b * E + e] = run;  // exclusive within the expert
-      run += c;
-    }
-    cnt[e] = run;
-  }
-  __syncthreads();
-  finish_counts(a, cnt, tmp, scalar);
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kCompactThreads)
-    for (int b = 0; b < a.blocks; ++b) a.blk_base[(int64_t)b * E + e] += tmp[e];
-}
-
-// Kernel 3: recompute the ranks and scatter.
+// Scatter of a compaction over several workgroups (the staging launch has
+// counted, and its last workgroup has turned the counts into per-workgroup
+// bases): recompute the ranks and write each route's position.
 __global__ __launch_bounds__(kCompactThreads) void compact_scatter_kernel(CompactArgs a) {
   extern __shared__ int lds[];
   const int E = a.num_experts;
@@ -84,18 +42,10 @@ __global__ __launch_bounds__(kCompactThreads) void compact_scatter_kernel(Compac
   scatter(a, blockIdx.x, hist, start, rank, expert);
 }
 
-int launch_compact(const CompactArgs& a, void* stream) {
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int E = a.num_experts;
-  if (a.blocks <= 1) {
-    hipLaunchKernelGGL(compact_fused_kernel, dim3(1), dim3(kCompactThreads), compact_one_workgroup_lds(E), s, a);
-  } else {
-    const size_t lds_hist = (size_t)(kCompactWaves * E + E) * 4;
-    const size_t lds_scan = (size_t)(E + E + 1 + 2) * 4;
-    hipLaunchKernelGGL(compact_count_kernel, dim3(a.blocks), dim3(kCompactThreads), lds_hist, s, a);
-    hipLaunchKernelGGL(compact_scan_kernel, dim3(1), dim3(kCompactThreads), lds_scan, s, a);
-    hipLaunchKernelGGL(compact_scatter_kernel, dim3(a.blocks), dim3(kCompactThreads), lds_hist, s, a);
-  }
+int launch_compact_scatter(const CompactArgs& a, void* stream) {
+  const size_t lds_hist = (size_t)(kCompactWaves * a.num_experts + a.num_experts) * 4;
+  hipLaunchKernelGGL(compact_scatter_kernel, dim3(a.blocks), dim3(kCompactThreads), lds_hist,
+                     static_cast<hipStream_t>(stream), a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

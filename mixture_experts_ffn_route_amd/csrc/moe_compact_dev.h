@@ -1,6 +1,6 @@
-// Device-side route compaction shared by the compaction kernels and the
-// fused stage kernel (route staging + single-workgroup compaction for small
-// batches).  See moe_compact.hip for the method.
+// Device-side route compaction, run by the staging launch (route staging
+// and counting, or the whole compaction for one workgroup) and by the
+// scatter kernel.  See moe_compact.hip for the method.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -12,7 +12,7 @@ namespace moe {
 
 constexpr int kCompactThreads = 256;
 constexpr int kCompactWaves = kCompactThreads / 64;
-constexpr int kItems = kCompactChunk / kCompactThreads;  // routes per lane per block
+constexpr int kItems = kCompactChunk / kCompactThreads;  // routes per lane per block (a.chunk <= kCompactChunk)
 
 __device__ __forceinline__ int id_bits(int num_experts) {
   int b = 0;
@@ -31,26 +31,29 @@ __device__ __forceinline__ uint64_t peers_of(int e, bool valid, int nbits) {
   return m;
 }
 
-// The routes a wave walks in block blk: the block's routes split into
-// kCompactWaves ascending contiguous ranges of whole 64-route items (at most
-// kItems each), so a small batch spreads over every wave.  Sweep and scatter
-// use the same split.
+// The routes a wave walks in block blk (routes [blk * chunk, blk * chunk +
+// chunk)): the block's routes split into kCompactWaves ascending contiguous
+// ranges of whole 64-route items (at most kItems each), so a small batch
+// spreads over every wave.  Sweep and scatter use the same split.  The last
+// wave's items may reach past the block's routes (a chunk of K=6 routes per
+// token is not a multiple of 256): `end` bounds them.
 struct WaveRange {
   int64_t base;
+  int64_t end;  // the block's last route + 1
   int items;
 };
 __device__ inline WaveRange wave_range(const CompactArgs& a, int blk, int wave) {
-  const int64_t b0 = (int64_t)blk * kCompactChunk;
-  const int64_t n = min((int64_t)a.routes - b0, (int64_t)kCompactChunk);
+  const int64_t b0 = (int64_t)blk * a.chunk;
+  const int64_t n = min((int64_t)a.routes - b0, (int64_t)a.chunk);
   const int items = (int)((n + 64 * kCompactWaves - 1) / (64 * kCompactWaves));
-  return WaveRange{b0 + (int64_t)wave * items * 64, items};
+  return WaveRange{b0 + (int64_t)wave * items * 64, b0 + n, items};
 }
 
 // Walk this block's routes wave by wave.  hist[w*E + e] holds wave w's
 // running count; rank[i] receives the count of same-expert routes before
-// item i within this wave's range.  ids_lds: the staged expert ids in LDS
-// (the fused staging kernel keeps them there), else they are read from
-// a.staged_idx.
+// item i within this wave's range.  ids_lds: the block's staged expert ids
+// in LDS, from its first route on (the staging launch keeps them there),
+// else they are read from a.staged_idx.
 __device__ inline void sweep(const CompactArgs& a, int blk, int* hist, int* rank, int* expert,
                              const int* ids_lds = nullptr) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -65,7 +68,7 @@ __device__ inline void sweep(const CompactArgs& a, int blk, int* hist, int* rank
   for (int it = 0; it < kItems; ++it) {
     const int64_t r = wr.base + it * 64 + lane;
     ids[it] = -1;
-    if (it < wr.items && r < a.routes) ids[it] = ids_lds ? ids_lds[r] : a.staged_idx[r];
+    if (it < wr.items && r < wr.end) ids[it] = ids_lds ? ids_lds[r - (int64_t)blk * a.chunk] : a.staged_idx[r];
   }
 #pragma unroll
   for (int it = 0; it < kItems; ++it) {
@@ -180,7 +183,7 @@ __device__ inline void scatter(const CompactArgs& a, int blk, int* hist, const i
   for (int it = 0; it < kItems; ++it) {
     if (it >= wr.items) break;
     const int64_t r = wr.base + it * 64 + lane;
-    if (r >= a.routes) continue;
+    if (r >= wr.end) continue;
     const int e = expert[it];
     int p = -1;
     if (e >= 0) {
@@ -195,8 +198,8 @@ __device__ inline void scatter(const CompactArgs& a, int blk, int* hist, const i
   }
 }
 
-// Single-workgroup compaction (routes <= kCompactChunk): count, scan,
-// scatter.  `lds` holds (kCompactWaves + 2) * E + 3 ints; ids_lds as in sweep.
+// Single-workgroup compaction (routes <= a.chunk): count, scan, scatter.
+// `lds` holds compact_one_workgroup_lds(E) bytes; ids_lds as in sweep.
 __device__ inline void compact_one_workgroup(const CompactArgs& a, int* lds, const int* ids_lds = nullptr) {
   const int E = a.num_experts;
   int* hist = lds;                        // [waves, E]
@@ -220,7 +223,78 @@ __device__ inline void compact_one_workgroup(const CompactArgs& a, int* lds, con
 }
 
 __host__ __device__ inline size_t compact_one_workgroup_lds(int num_experts) {
-  return (size_t)(kCompactWaves * num_experts + num_experts + num_experts + 1 + 2) * 4;
+  return (size_t)(kCompactWaves * num_experts + num_experts + num_experts + 1 + 3) * 4;
+}
+
+// Values one compaction workgroup hands to another within a launch: stored
+// write-through and loaded from the device-coherent level (agent scope), so
+// that no cache-wide writeback or invalidate is needed between them.
+__device__ __forceinline__ void store_agent(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t load_agent(int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Compaction over several workgroups, all but the scatter (which needs
+// every workgroup's bases, so it is a launch of its own): workgroup blk
+// counts its routes per expert and publishes the counts and its route rows'
+// status bits.  The workgroup whose arrival completes the count writes the
+// header (tokens, every workgroup's status bits), turns the counts into
+// offsets, per-workgroup bases and the tile list, and returns the arrival
+// counter to zero.
+//
+// Ordering: each wave waits until its write-through stores are complete
+// before the workgroup barrier, the arrival is an agent-scope atomic after
+// it, and the completing workgroup loads the counts at agent scope after its
+// atomic has returned.  No workgroup waits for another.
+__device__ inline void count_and_arrive(const CompactArgs& a, int blk, int* lds, const int* ids_lds,
+                                        uint32_t status, int32_t tokens) {
+  const int E = a.num_experts;
+  int* hist = lds;                        // [waves, E]
+  int* cnt = hist + kCompactWaves * E;    // [E]
+  int* tmp = cnt + E;                     // [E + 1]
+  int* scalar = tmp + E + 1;              // [3]
+  int rank[kItems], expert[kItems];
+  clear_hist(hist, kCompactWaves * E);
+  __syncthreads();
+  sweep(a, blk, hist, rank, expert, ids_lds);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kCompactThreads) {
+    int s = 0;
+    for (int w = 0; w < kCompactWaves; ++w) s += hist[w * E + e];
+    store_agent(a.blk_base + (int64_t)blk * E + e, s);
+  }
+  if (threadIdx.x == 0) store_agent(reinterpret_cast<int32_t*>(a.blk_status) + blk, (int32_t)status);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0)
+    scalar[2] = __hip_atomic_fetch_add(a.arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.blocks - 1;
+  __syncthreads();
+  if (!scalar[2]) return;
+  // the last arrival: header, then the scan over workgroups
+  if (threadIdx.x < 64) {
+    uint32_t v = 0;
+    if (threadIdx.x == kHdrStatus)
+      for (int b = 0; b < a.blocks; ++b) v |= (uint32_t)load_agent(reinterpret_cast<int32_t*>(a.blk_status) + b);
+    if (threadIdx.x == kHdrTokens) v = (uint32_t)tokens;
+    a.hdr[threadIdx.x] = v;
+  }
+  for (int e = threadIdx.x; e < E; e += kCompactThreads) {
+    int run = 0;
+    for (int b = 0; b < a.blocks; ++b) {
+      const int c = load_agent(a.blk_base + (int64_t)b * E + e);
+      a.blk_base[(int64_t)b * E + e] = run;  // exclusive within the expert
+      run += c;
+    }
+    cnt[e] = run;
+  }
+  __syncthreads();
+  finish_counts(a, cnt, tmp, scalar);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kCompactThreads)
+    for (int b = 0; b < a.blocks; ++b) a.blk_base[(int64_t)b * E + e] += tmp[e];
+  if (threadIdx.x == 0) store_agent(a.arrive, 0);  // as the arrivals do, at the device-coherent level
 }
 
 }  // namespace moe

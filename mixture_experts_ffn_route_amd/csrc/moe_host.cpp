@@ -119,7 +119,7 @@ Layout compute_layout(const moe_config_t& cfg, const Tactic& t, int32_t max_rows
   L.row_cap = cap >= (double)L.route_slots ? L.route_slots : (int64_t)cap;
   if (L.row_cap < 1) L.row_cap = 1;
   L.max_m_tiles = (L.row_cap + t.block_m - 1) / t.block_m + E;
-  L.compact_blocks = (L.route_slots + kCompactChunk - 1) / kCompactChunk;
+  L.compact_blocks = compact_blocks_for(max_rows, cfg.top_k);
 
   L.size[MOE_REGION_STATUS] = 256;
   L.size[MOE_REGION_STAGED_IDX] = L.route_slots * 4;
@@ -143,7 +143,8 @@ Layout compute_layout(const moe_config_t& cfg, const Tactic& t, int32_t max_rows
   L.size[MOE_REGION_GATEUP] = (cfg.flags & MOE_FLAG_UNFUSED_FC1) ? L.row_cap * 2 * I * 4 : 0;
   L.size[MOE_REGION_READY] = (cfg.flags & MOE_FLAG_PERSISTENT_FFN) ? L.max_m_tiles * 4 : 0;
   L.size[MOE_REGION_ARRIVE] = (cfg.flags & MOE_FLAG_FUSED_COMBINE) ? (int64_t)max_rows * ((H + 255) / 256) * 4 : 0;
-  L.size[kRegionBlkBase] = L.compact_blocks * E * 4;
+  // compaction: per-(workgroup, expert) bases, per-workgroup status bits, the arrival counter
+  L.size[kRegionBlkBase] = (L.compact_blocks * (E + 1) + 1) * 4;
   size_t off = 0;
   for (int r = 0; r < kNumRegions; ++r) {
     L.off[r] = off;

@@ -10,8 +10,7 @@
 namespace moe {
 
 constexpr int kMaxExperts = 1024;
-constexpr int kCompactChunk = 4096;  // routes per compaction workgroup (256 lanes x 16)
-constexpr int kFuseRoutes = 2048;    // staging and compaction share one launch up to this many routes
+constexpr int kCompactChunk = 4096;  // bound on the routes per compaction workgroup (256 lanes x 16)
 constexpr int kNumRegions = 21;
 constexpr int kRegionBlkBase = 20;   // internal: per-(compaction block, expert) bases
 
@@ -35,7 +34,7 @@ struct Layout {
   int64_t route_slots;  // max_rows * K
   int64_t row_cap;      // route rows held by h/y
   int64_t max_m_tiles;  // bound on the tile list length
-  int64_t compact_blocks;
+  int64_t compact_blocks;  // compaction workgroups at max_rows tokens
   size_t off[kNumRegions];
   size_t size[kNumRegions];
   size_t total;
@@ -43,6 +42,15 @@ struct Layout {
 
 // Host-only logic (moe_host.cpp, no HIP dependency).
 int32_t token_bucket(int32_t tokens);
+// Tokens per compaction workgroup: whole tokens, at most kCompactChunk routes.
+inline int32_t compact_chunk_tokens(int32_t top_k) { return kCompactChunk / top_k; }
+// Compaction workgroups for `tokens` staged tokens (at least one, which also
+// resets the header when no token is staged).
+inline int32_t compact_blocks_for(int64_t tokens, int32_t top_k) {
+  const int64_t tc = compact_chunk_tokens(top_k);
+  const int64_t b = (tokens + tc - 1) / tc;
+  return b < 1 ? 1 : (int32_t)b;
+}
 // Limits that depend on the layout (call after compute_layout).
 moe_status_t validate_layout(const moe_config_t& cfg, const Layout& L);
 moe_status_t validate_config(const moe_config_t* cfg, int32_t expected_m, int32_t max_rows,
@@ -72,7 +80,11 @@ struct StageArgs {
   int64_t x_plane;        // MX variant: bytes from the hi-term plane to the lo-term plane
   uint32_t* xs_mx;        // MX variant: packed E8M0 exponents [rows, H/32] (byte 0 hi, byte 1 lo)
 };
-int launch_stage(const StageArgs& a, void* stream);
+struct CompactArgs;
+// One launch stages the batch: the first c.blocks workgroups stage and check
+// the route rows and compact them (the whole compaction when c.blocks == 1,
+// else everything but the scatter), the others quantise (or split) x.
+int launch_stage(const StageArgs& a, const CompactArgs& c, void* stream);
 
 struct CompactArgs {
   const int32_t* staged_idx;
@@ -81,8 +93,11 @@ struct CompactArgs {
   int32_t row_cap;
   int32_t block_m;
   int32_t blocks;          // compaction workgroups
+  int32_t chunk;           // routes per workgroup: compact_chunk_tokens(K) * K
   uint32_t* hdr;
   int32_t* blk_base;       // [blocks, E]
+  uint32_t* blk_status;    // [blocks] MOE_DEV_* bits of each workgroup's route rows
+  int32_t* arrive;         // one word, zero between launches: compaction workgroups done counting
   int32_t* counts;         // [E]
   int32_t* offsets;        // [E+1]
   int32_t* sorted_route;   // [row_cap]
@@ -90,9 +105,8 @@ struct CompactArgs {
   int32_t* tiles;          // [max_m_tiles, 4] (expert, first sorted row, rows, only-tile flag)
   int32_t* ready;          // [max_m_tiles] persistent FC1->FC2 counters, zeroed per listed tile (or null)
 };
-int launch_compact(const CompactArgs& a, void* stream);
-// Stage and compact in one launch (routes <= kCompactChunk).
-int launch_stage_compact(const StageArgs& a, const CompactArgs& c, void* stream);
+// Scatter of a compaction split over several workgroups (after launch_stage).
+int launch_compact_scatter(const CompactArgs& a, void* stream);
 
 // Operands of the last-arriver combine fused into FC2 (moe_combine_dev.h).
 struct FusedCombineArgs {

@@ -15,7 +15,6 @@ namespace moe {
 // One 16-lane group per 1x128 block; each lane owns 8 consecutive columns.
 //   s = amax / 448 (IEEE float division), q = RNE_sat(x / s), s == 0 -> q = 0.
 // With a prequantised input (x_scale != null) codes and scales are copied.
-// Block 0 also resets the device header for this batch.
 __device__ inline void quant_1x128(const StageArgs& a, int64_t g, int64_t groups, int copies) {
   const int64_t grp = g >> 4;
   if (grp >= groups) return;
@@ -100,9 +99,10 @@ __device__ inline void split_mx(const StageArgs& a, int64_t g, int64_t groups) {
 
 // One thread per token slot row in [0, max_rows).  Live rows are checked and
 // masked; rows past the live count are staged as masked.  ids_lds (live rows
-// only): a copy of the staged expert ids for the compaction of the same
-// workgroup.
-__device__ inline void stage_route_row(const StageArgs& a, int t, int* ids_lds = nullptr) {
+// only, from token t0 on): a copy of the staged expert ids for the
+// compaction of the same workgroup.  Status bits go to the workgroup's LDS
+// word `status`.
+__device__ inline void stage_route_row(const StageArgs& a, int t, int* ids_lds, int t0, uint32_t* status) {
   const int K = a.top_k;
   uint32_t bits = 0;
   int ids[8];
@@ -160,54 +160,48 @@ __device__ inline void stage_route_row(const StageArgs& a, int t, int* ids_lds =
     if (k < K) {
       a.staged_idx[(int64_t)t * K + k] = act[k] ? ids[k] : -1;
       a.staged_w[(int64_t)t * K + k] = act[k] ? ws[k] : 0.0f;
-      if (ids_lds && t < a.tokens) ids_lds[t * K + k] = act[k] ? ids[k] : -1;
+      if (ids_lds && t < a.tokens) ids_lds[(t - t0) * K + k] = act[k] ? ids[k] : -1;
     }
   }
-  if (bits) atomicOr(a.hdr + kHdrStatus, bits);
+  if (bits) atomicOr(status, bits);
 }
 
-__device__ inline void reset_header(const StageArgs& a) {
-  if (threadIdx.x < 64) a.hdr[threadIdx.x] = threadIdx.x == kHdrTokens ? (uint32_t)a.tokens : 0u;
-}
-
-__global__ __launch_bounds__(256) void stage_quant_kernel(StageArgs a, int64_t groups, int copies) {
-  if (blockIdx.x == 0) reset_header(a);
-  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (a.act_format == MOE_ACT_BF16)
-    split_mx(a, g, groups);
-  else
-    quant_1x128(a, g, groups, copies);
-}
-
-// One thread per token slot row in [0, max_rows).  Runs after the header reset
-// of stage_quant_kernel (same stream).
-__global__ __launch_bounds__(256) void stage_routes_kernel(StageArgs a) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t < a.max_rows) stage_route_row(a, t);
-}
-
-// Small batches (routes <= kFuseRoutes): one launch stages everything.
-// Blocks [0, quant_blocks) quantise (or split) x; the last block resets the
-// header, stages and checks every route row, then compacts the routes as a
-// single workgroup, so the forward starts at FC1.
-__global__ __launch_bounds__(256) void stage_fused_kernel(StageArgs a, CompactArgs c, int64_t groups, int copies,
-                                                          int quant_blocks) {
+// The staging launch.  Workgroups [0, c.blocks) take the route rows, one
+// chunk of whole tokens each, and compact them: the whole compaction when
+// c.blocks == 1, else the counting (compact_scatter_kernel finishes in the
+// next launch).  They come first so that they run beside the quantisation
+// workgroups [c.blocks, ...), which are most of the grid.  The header is
+// written by the compaction (after every status bit of the launch is known);
+// nothing else in the launch touches it.
+__global__ __launch_bounds__(256) void stage_kernel(StageArgs a, CompactArgs c, int64_t groups, int copies) {
   extern __shared__ int lds[];
-  if ((int)blockIdx.x < quant_blocks) {
-    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if ((int)blockIdx.x >= c.blocks) {
+    const int64_t g = (int64_t)(blockIdx.x - c.blocks) * 256 + threadIdx.x;
     if (a.act_format == MOE_ACT_BF16)
       split_mx(a, g, groups);
     else
       quant_1x128(a, g, groups, copies);
     return;
   }
-  // the staged ids of the live rows stay in LDS for the compaction
-  int* ids_lds = lds + compact_one_workgroup_lds(c.num_experts) / 4;
-  reset_header(a);
+  const int blk = blockIdx.x;
+  int* ids_lds = lds + compact_one_workgroup_lds(c.num_experts) / 4;  // [c.chunk]
+  uint32_t* status = reinterpret_cast<uint32_t*>(ids_lds + c.chunk);
+  if (threadIdx.x == 0) *status = 0u;
   __syncthreads();
-  for (int t = threadIdx.x; t < a.max_rows; t += 256) stage_route_row(a, t, ids_lds);
+  const int tc = c.chunk / a.top_k;
+  const int t0 = blk * tc, t1 = min(t0 + tc, a.tokens);
+  for (int t = t0 + (int)threadIdx.x; t < t1; t += 256) stage_route_row(a, t, ids_lds, t0, status);
+  for (int t = a.tokens + blk * 256 + (int)threadIdx.x; t < a.max_rows; t += c.blocks * 256)
+    stage_route_row(a, t, nullptr, 0, status);  // rows past the live count
   __syncthreads();
-  compact_one_workgroup(c, lds, ids_lds);
+  if (c.blocks == 1) {
+    if (threadIdx.x < 64)
+      a.hdr[threadIdx.x] = threadIdx.x == kHdrTokens ? (uint32_t)a.tokens : threadIdx.x == kHdrStatus ? *status : 0u;
+    __syncthreads();
+    compact_one_workgroup(c, lds, ids_lds);
+  } else {
+    count_and_arrive(c, blk, lds, ids_lds, *status, a.tokens);
+  }
 }
 
 static void quant_grid(const StageArgs& a, int64_t* groups, int* blocks, int* copies) {
@@ -221,23 +215,13 @@ static void quant_grid(const StageArgs& a, int64_t* groups, int* blocks, int* co
   *copies = (a.flags & MOE_FLAG_PER_ROUTE_STAGING) ? a.top_k : 1;
 }
 
-int launch_stage(const StageArgs& a, void* stream) {
-  hipStream_t s = static_cast<hipStream_t>(stream);
+int launch_stage(const StageArgs& a, const CompactArgs& c, void* stream) {
   int64_t groups;
   int qblocks, copies;
   quant_grid(a, &groups, &qblocks, &copies);
-  hipLaunchKernelGGL(stage_quant_kernel, dim3(qblocks > 0 ? qblocks : 1), dim3(256), 0, s, a, groups, copies);
-  hipLaunchKernelGGL(stage_routes_kernel, dim3((a.max_rows + 255) / 256), dim3(256), 0, s, a);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-int launch_stage_compact(const StageArgs& a, const CompactArgs& c, void* stream) {
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  int64_t groups;
-  int qblocks, copies;
-  quant_grid(a, &groups, &qblocks, &copies);
-  const size_t lds = compact_one_workgroup_lds(c.num_experts) + (size_t)c.routes * 4;
-  hipLaunchKernelGGL(stage_fused_kernel, dim3(qblocks + 1), dim3(256), lds, s, a, c, groups, copies, qblocks);
+  const size_t lds = compact_one_workgroup_lds(c.num_experts) + (size_t)c.chunk * 4 + 4;
+  hipLaunchKernelGGL(stage_kernel, dim3(c.blocks + qblocks), dim3(256), lds, static_cast<hipStream_t>(stream), a, c,
+                     groups, copies);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -109,6 +109,29 @@ def test_ragged_token_counts(tokens):
         assert_output_close(_bits(out), res.out_bits, f"T={tokens}")
 
 
+def test_multi_workgroup_compaction_repeated():
+    """Route compaction over several workgroups (whole tokens each, at most
+    4096 routes: 682 tokens per workgroup at K=6) in consecutive stagings
+    whose workgroup count changes (4, 2, 2, 1, 4).  The last workgroup to
+    finish counting writes the header and the tile list and returns the
+    arrival counter to zero; a counter left elsewhere would leave the next
+    staging without its scan."""
+    shape = MoEShape(2100, 256, 128, 16, 6, "topk")
+    inp = make_layer_inputs(shape, seed=41, masked_fraction=0.2)
+    dev = to_device(inp)
+    layer = make_layer(shape, dev, max_rows=2100)
+    for T in (2100, 700, 683, 1, 2100):
+        out = run_forward(layer, dev, tokens=T)
+        torch.cuda.synchronize()
+        res = M.forward_fp8(inp.x_bf16[:T], inp.topk_idx[:T], inp.topk_w[:T], inp.w13, inp.w13_scale, inp.w2,
+                            inp.w2_scale)
+        _check_compaction(layer, res, shape, T)
+        assert layer.status() == res.status, T
+        sidx = _np(layer.region("staged_idx", torch.int32))
+        assert np.all(sidx[T * 6:2100 * 6] == -1)
+        assert_output_close(_bits(out), res.out_bits, f"T={T}")
+
+
 @pytest.mark.parametrize("pair", [(8, 48), (2, 24), (96, 4096), (128, 200), (8, 4096)])
 def test_tactics_agree_bit_exact(pair):
     """Every token tile (16 to 256 tokens) computes the same bits: each
