@@ -82,7 +82,7 @@ moe::CompactArgs compact_args(moe_layer* l, int32_t T) {
   ca.row_cap = (int32_t)l->L.row_cap;
   ca.block_m = l->tac.block_m;
   ca.blocks = moe::compact_blocks_for(T, l->cfg.top_k);
-  ca.chunk = moe::compact_chunk_tokens(l->cfg.top_k) * l->cfg.top_k;
+  ca.chunk = moe::compact_chunk_routes(T, l->cfg.top_k);
   ca.hdr = region<uint32_t>(l, MOE_REGION_STATUS);
   // internal region: bases [compact_blocks, E], status [compact_blocks], arrival counter
   ca.blk_base = region<int32_t>(l, moe::kRegionBlkBase);

@@ -13,6 +13,8 @@ namespace moe {
 constexpr int kCompactThreads = 256;
 constexpr int kCompactWaves = kCompactThreads / 64;
 constexpr int kItems = kCompactChunk / kCompactThreads;  // routes per lane per block (a.chunk <= kCompactChunk)
+static_assert(kCompactOneRoutes <= kCompactChunk && kCompactBlockRoutes <= kCompactChunk && kCompactBlockRoutes >= 8,
+              "a compaction workgroup holds at most kCompactChunk routes and at least one token of 8");
 
 __device__ __forceinline__ int id_bits(int num_experts) {
   int b = 0;
@@ -272,28 +274,54 @@ __device__ inline void count_and_arrive(const CompactArgs& a, int blk, int* lds,
     scalar[2] = __hip_atomic_fetch_add(a.arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.blocks - 1;
   __syncthreads();
   if (!scalar[2]) return;
-  // the last arrival: header, then the scan over workgroups
+  // The last arrival: header, then the scan over workgroups.  Each loop
+  // over workgroups loads 8 of them at once, so its round trips are
+  // blocks / 8, not blocks.
+  constexpr int kBatch = 8;
   if (threadIdx.x < 64) {
     uint32_t v = 0;
-    if (threadIdx.x == kHdrStatus)
-      for (int b = 0; b < a.blocks; ++b) v |= (uint32_t)load_agent(reinterpret_cast<int32_t*>(a.blk_status) + b);
+    if (threadIdx.x == kHdrStatus) {
+      for (int b0 = 0; b0 < a.blocks; b0 += kBatch) {
+        int32_t st[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+          st[j] = b0 + j < a.blocks ? load_agent(reinterpret_cast<int32_t*>(a.blk_status) + b0 + j) : 0;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) v |= (uint32_t)st[j];
+      }
+    }
     if (threadIdx.x == kHdrTokens) v = (uint32_t)tokens;
     a.hdr[threadIdx.x] = v;
   }
   for (int e = threadIdx.x; e < E; e += kCompactThreads) {
     int run = 0;
-    for (int b = 0; b < a.blocks; ++b) {
-      const int c = load_agent(a.blk_base + (int64_t)b * E + e);
-      a.blk_base[(int64_t)b * E + e] = run;  // exclusive within the expert
-      run += c;
+    for (int b0 = 0; b0 < a.blocks; b0 += kBatch) {
+      int c[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) c[j] = b0 + j < a.blocks ? load_agent(a.blk_base + (int64_t)(b0 + j) * E + e) : 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) run += c[j];
     }
     cnt[e] = run;
   }
   __syncthreads();
   finish_counts(a, cnt, tmp, scalar);
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kCompactThreads)
-    for (int b = 0; b < a.blocks; ++b) a.blk_base[(int64_t)b * E + e] += tmp[e];
+  // each workgroup's first position per expert: the expert's offset plus the
+  // counts of the workgroups before it
+  for (int e = threadIdx.x; e < E; e += kCompactThreads) {
+    int run = tmp[e];
+    for (int b0 = 0; b0 < a.blocks; b0 += kBatch) {
+      int c[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) c[j] = b0 + j < a.blocks ? load_agent(a.blk_base + (int64_t)(b0 + j) * E + e) : 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (b0 + j < a.blocks) a.blk_base[(int64_t)(b0 + j) * E + e] = run;
+        run += c[j];
+      }
+    }
+  }
   if (threadIdx.x == 0) store_agent(a.arrive, 0);  // as the arrivals do, at the device-coherent level
 }
 

@@ -10,7 +10,9 @@
 namespace moe {
 
 constexpr int kMaxExperts = 1024;
-constexpr int kCompactChunk = 4096;  // bound on the routes per compaction workgroup (256 lanes x 16)
+constexpr int kCompactChunk = 4096;        // bound on the routes per compaction workgroup (256 lanes x 16)
+constexpr int kCompactOneRoutes = 2048;    // batches up to this many routes compact in one workgroup
+constexpr int kCompactBlockRoutes = 1024;  // beyond that, about this many routes per workgroup
 constexpr int kNumRegions = 21;
 constexpr int kRegionBlkBase = 20;   // internal: per-(compaction block, expert) bases
 
@@ -42,14 +44,20 @@ struct Layout {
 
 // Host-only logic (moe_host.cpp, no HIP dependency).
 int32_t token_bucket(int32_t tokens);
-// Tokens per compaction workgroup: whole tokens, at most kCompactChunk routes.
-inline int32_t compact_chunk_tokens(int32_t top_k) { return kCompactChunk / top_k; }
-// Compaction workgroups for `tokens` staged tokens (at least one, which also
-// resets the header when no token is staged).
+// Tokens per compaction workgroup when there are several: whole tokens,
+// at most kCompactBlockRoutes routes.
+inline int32_t compact_chunk_tokens(int32_t top_k) { return kCompactBlockRoutes / top_k; }
+// Compaction workgroups for `tokens` staged tokens: one (which also writes
+// the header when no token is staged) up to kCompactOneRoutes routes.
 inline int32_t compact_blocks_for(int64_t tokens, int32_t top_k) {
+  if (tokens * top_k <= kCompactOneRoutes) return 1;
   const int64_t tc = compact_chunk_tokens(top_k);
-  const int64_t b = (tokens + tc - 1) / tc;
-  return b < 1 ? 1 : (int32_t)b;
+  return (int32_t)((tokens + tc - 1) / tc);
+}
+// Routes per compaction workgroup (the whole batch for one workgroup).
+inline int32_t compact_chunk_routes(int64_t tokens, int32_t top_k) {
+  if (tokens * top_k <= kCompactOneRoutes) return tokens > 0 ? (int32_t)(tokens * top_k) : top_k;
+  return compact_chunk_tokens(top_k) * top_k;
 }
 // Limits that depend on the layout (call after compute_layout).
 moe_status_t validate_layout(const moe_config_t& cfg, const Layout& L);
@@ -93,7 +101,7 @@ struct CompactArgs {
   int32_t row_cap;
   int32_t block_m;
   int32_t blocks;          // compaction workgroups
-  int32_t chunk;           // routes per workgroup: compact_chunk_tokens(K) * K
+  int32_t chunk;           // routes per workgroup (whole tokens, <= kCompactChunk): compact_chunk_routes
   uint32_t* hdr;
   int32_t* blk_base;       // [blocks, E]
   uint32_t* blk_status;    // [blocks] MOE_DEV_* bits of each workgroup's route rows
