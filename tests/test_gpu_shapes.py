@@ -3,7 +3,7 @@
 The named configurations exercise K in {2, 6, 8} and E in {8, 32}; here every
 supported top-k (1, 2, 4, 6, 8), expert counts from 1 to 1024, H and I from
 one to nine 128-column blocks (odd block counts leave the last FC2 column
-tile half full), token counts from 1 to 600 (all three compaction paths), several FC2 tiles
+tile half full), token counts from 1 to 600 (one and several compaction workgroups), several FC2 tiles
 per workgroup (each tile's output stores still in flight while the next
 tile's first stages are awaited), masked routes and both weight formats are
 compared with the float64 oracle:
@@ -38,8 +38,8 @@ def _shapes():
         (33, 384, 384, 257, 8, 0.3, False),
         (1, 128, 256, 8, 8, 0.0, True),
         (130, 384, 128, 1024, 2, 0.0, False),  # the largest expert count
-        (300, 256, 128, 33, 8, 0.3, False),    # 2400 routes: compaction in its own launch
-        (600, 128, 128, 9, 8, 0.0, False),     # 4800 routes: multi-workgroup compaction
+        (300, 256, 128, 33, 8, 0.3, False),    # 2400 routes: three compaction workgroups
+        (600, 128, 128, 9, 8, 0.0, False),     # 4800 routes: five compaction workgroups
         (600, 256, 256, 12, 8, 0.3, True),
         # several FC2 tiles per workgroup, so a tile's first waits run while
         # the previous tile's output stores are in flight
