@@ -195,8 +195,8 @@ enum {
 
 /* Kernel classes timed by the optional profiler. */
 enum {
-  MOE_KERNEL_STAGE = 0,
-  MOE_KERNEL_COMPACT = 1,
+  MOE_KERNEL_STAGE = 0,    /* the staging launch: quantisation, route staging, compaction counts */
+  MOE_KERNEL_COMPACT = 1,  /* the compaction's scatter, when it is a launch of its own */
   MOE_KERNEL_FC1 = 2,
   MOE_KERNEL_FC2 = 3,
   MOE_KERNEL_COMBINE = 4,
@@ -251,12 +251,15 @@ moe_status_t moe_layer_create(const moe_config_t* cfg, int32_t expected_m, int32
  *  num_tokens T, 0 <= T <= max_rows (else MOE_ERR_CAPACITY).
  *  out_bf16   device bfloat16 [T, H], written by the next moe_layer_forward.
  * The caller's tensors are never modified.  Rows [T, max_rows) of the staged
- * routes are masked. */
+ * routes are masked.  The same launch counts the staged routes per expert
+ * and builds the row-tile list; for batches of up to 2048 routes it also
+ * finishes the compaction (the per-route positions). */
 moe_status_t moe_stage_inputs(moe_layer_t* layer, const void* x, const float* x_scale,
                               const int32_t* topk_idx, const float* topk_w, int32_t num_tokens,
                               void* out_bf16, void* stream);
 
-/* Run compact -> FC1(+SwiGLU+requant) -> FC2 -> combine on the staged batch
+/* Run the rest of the compaction (the per-route positions, for batches over
+ * 2048 routes) -> FC1(+SwiGLU+requant) -> FC2 -> combine on the staged batch
  * (with MOE_FLAG_FUSED_COMBINE the combine runs inside FC2).
  * Stream-ordered, no host synchronisation (PR #4069, Description: no
  * host-side synchronization in the steady-state forward). */

@@ -65,7 +65,7 @@ __device__ inline void quant_1x128(const StageArgs& a, int64_t g, int64_t groups
 // can consume them: hi = e4m3(x / 2^e_hi), lo = e4m3((x - hi * 2^e_hi) / 2^e_lo).
 // Four lanes per 32-column block, eight columns each.  Writes the hi codes
 // to plane 0, the lo codes to plane 1 (x_plane bytes further) and one word
-// (e_hi + 127) | (e_lo + 127) << 8 per block.  Block 0 resets the header.
+// (e_hi + 127) | (e_lo + 127) << 8 per block.
 __device__ inline void split_mx(const StageArgs& a, int64_t g, int64_t groups) {
   const int64_t grp = g >> 2;
   if (grp >= groups) return;
