@@ -146,6 +146,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens for the CPU oracle baseline (0: skip)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (reference for HBM byte counters)")
+    ap.add_argument("--expected-m", type=int, default=None,
+                    help="expected rows per expert, which picks the token tile (default: T*K/E)")
     ap.add_argument("--sweep", default="", help="comma-separated token counts; extra lines to --sweep-out")
     ap.add_argument("--sweep-out", default="gpurun_out/sweep.jsonl")
     args = ap.parse_args()
@@ -179,7 +181,7 @@ def main():
         inp = make_layer_inputs(shape, seed=args.seed, weight_format=args.weights)
         log(f"[bench] generated T={tokens} inputs in {time.perf_counter() - t0:.1f}s")
         dev = to_device(inp)
-        layer = make_layer(shape, dev, mx=mx, flags=flags)
+        layer = make_layer(shape, dev, mx=mx, flags=flags, expected_m=args.expected_m)
         out = torch.empty((tokens, shape.hidden), dtype=torch.bfloat16, device="cuda")
 
         def step():
