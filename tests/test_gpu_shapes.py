@@ -46,6 +46,9 @@ def _shapes():
         (128, 2048, 512, 256, 8, 0.3, False),  # 16-token tiles, 2048 FC2 tiles
         (40, 4096, 1024, 64, 8, 0.0, False),   # 16-token tiles, 1024 FC2 tiles
         (400, 4096, 384, 32, 8, 0.0, False),   # 128-token tiles, three-stage ring, 512 FC2 tiles
+        # compaction over several workgroups: the largest expert count, and one route per token
+        (1100, 128, 128, 1024, 2, 0.2, False),  # 2200 routes, 3 workgroups, 1024 experts
+        (2500, 128, 256, 8, 1, 0.0, True),      # 2500 routes, 3 workgroups
     ]
     return [(MoEShape(T, H, I, E, K, "topk"), m, mx, 100 + i) for i, (T, H, I, E, K, m, mx) in enumerate(table)]
 
