@@ -13,7 +13,8 @@
 namespace moe {
 
 // One 16-lane group per 1x128 block; each lane owns 8 consecutive columns.
-//   s = amax / 448 (IEEE float division), q = RNE_sat(x / s), s == 0 -> q = 0.
+//   s = amax / 448 (IEEE float division), q = RNE_sat(x / s), s == 0 -> q = 0
+// (the codes of the IEEE quotient x / s; see below for how it is formed).
 // With a prequantised input (x_scale != null) codes and scales are copied.
 __device__ inline void quant_1x128(const StageArgs& a, int64_t g, int64_t groups, int copies) {
   const int64_t grp = g >> 4;
@@ -40,9 +41,24 @@ __device__ inline void quant_1x128(const StageArgs& a, int64_t g, int64_t groups
     if (s == 0.0f) {
       codes = make_uint2(0u, 0u);
     } else {
+      // x / s without eight IEEE divisions: inv = fl32(1/s) once, then per
+      // element q0 = fl32(x * inv), r = fma(-q0, s, x) and q = fma(r, inv, q0)
+      // (a reciprocal with one correction step).  For every bf16 x with
+      // |x| <= amax and every block with s >= 2^-90 this gives the e4m3 code
+      // of the IEEE quotient, checked exhaustively; below that (amax under
+      // ~3.6e-25) the remainder can underflow, so such blocks divide.
       float q[8];
+      if (s >= 0x1p-90f) {
+        const float inv = 1.0f / s;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = v[i] / s;
+        for (int i = 0; i < 8; ++i) {
+          const float q0 = v[i] * inv;
+          q[i] = fmaf(fmaf(-q0, s, v[i]), inv, q0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = v[i] / s;
+      }
       int w0 = cvt2_e4m3(q[0], q[1], 0, false);
       w0 = cvt2_e4m3(q[2], q[3], w0, true);
       int w1 = cvt2_e4m3(q[4], q[5], 0, false);
