@@ -12,67 +12,73 @@
 
 namespace moe {
 
-// One 16-lane group per 1x128 block; each lane owns 8 consecutive columns.
+// One 8-lane group per 1x128 block; each lane owns 16 consecutive columns.
 //   s = amax / 448 (IEEE float division), q = RNE_sat(x / s), s == 0 -> q = 0
 // (the codes of the IEEE quotient x / s; see below for how it is formed).
 // With a prequantised input (x_scale != null) codes and scales are copied.
+constexpr int kQuantLanes = 8;  // lanes per 1x128 block
 __device__ inline void quant_1x128(const StageArgs& a, int64_t g, int64_t groups, int copies) {
-  const int64_t grp = g >> 4;
+  const int64_t grp = g / kQuantLanes;
   if (grp >= groups) return;
-  const int lane16 = threadIdx.x & 15;
+  const int ql = threadIdx.x & (kQuantLanes - 1);
   const int kbs = a.hidden >> 7;
   const int64_t row = grp / kbs;
   const int kb = (int)(grp - row * kbs);
-  const int64_t col = (int64_t)kb * 128 + lane16 * 8;
-  uint2 codes;
+  const int64_t col = (int64_t)kb * 128 + ql * 16;
+  uint4 codes;
   float s;
   if (a.x_scale == nullptr) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + row * a.hidden + col);
-    float v[8];
-    v[0] = bf16_to_f32(raw.x & 0xffffu); v[1] = bf16_to_f32(raw.x >> 16);
-    v[2] = bf16_to_f32(raw.y & 0xffffu); v[3] = bf16_to_f32(raw.y >> 16);
-    v[4] = bf16_to_f32(raw.z & 0xffffu); v[5] = bf16_to_f32(raw.z >> 16);
-    v[6] = bf16_to_f32(raw.w & 0xffffu); v[7] = bf16_to_f32(raw.w >> 16);
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + row * a.hidden + col);
+    const uint4 r0 = src[0], r1 = src[1];
+    const uint32_t words[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = bf16_to_f32(words[i] & 0xffffu);
+      v[2 * i + 1] = bf16_to_f32(words[i] >> 16);
+    }
     float m = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
-    m = group_max<16>(m);
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+    m = group_max<kQuantLanes>(m);
     s = m / kE4m3Max;
     if (s == 0.0f) {
-      codes = make_uint2(0u, 0u);
+      codes = make_uint4(0u, 0u, 0u, 0u);
     } else {
-      // x / s without eight IEEE divisions: inv = fl32(1/s) once, then per
-      // element q0 = fl32(x * inv), r = fma(-q0, s, x) and q = fma(r, inv, q0)
+      // x / s without an IEEE division per element: inv = fl32(1/s) once,
+      // then q0 = fl32(x * inv), r = fma(-q0, s, x) and q = fma(r, inv, q0)
       // (a reciprocal with one correction step).  For every bf16 x with
       // |x| <= amax and every block with s >= 2^-90 this gives the e4m3 code
       // of the IEEE quotient, checked exhaustively; below that (amax under
       // ~3.6e-25) the remainder can underflow, so such blocks divide.
-      float q[8];
+      float q[16];
       if (s >= 0x1p-90f) {
         const float inv = 1.0f / s;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 16; ++i) {
           const float q0 = v[i] * inv;
           q[i] = fmaf(fmaf(-q0, s, v[i]), inv, q0);
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = v[i] / s;
+        for (int i = 0; i < 16; ++i) q[i] = v[i] / s;
       }
-      int w0 = cvt2_e4m3(q[0], q[1], 0, false);
-      w0 = cvt2_e4m3(q[2], q[3], w0, true);
-      int w1 = cvt2_e4m3(q[4], q[5], 0, false);
-      w1 = cvt2_e4m3(q[6], q[7], w1, true);
-      codes = make_uint2((uint32_t)w0, (uint32_t)w1);
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        int c = cvt2_e4m3(q[4 * j], q[4 * j + 1], 0, false);
+        w[j] = (uint32_t)cvt2_e4m3(q[4 * j + 2], q[4 * j + 3], c, true);
+      }
+      codes = make_uint4(w[0], w[1], w[2], w[3]);
     }
   } else {
-    codes = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(a.x) + row * a.hidden + col);
+    codes = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.x) + row * a.hidden + col);
     s = a.x_scale[row * kbs + kb];
   }
   for (int c = 0; c < copies; ++c) {
     const int64_t dst = row * copies + c;
-    *reinterpret_cast<uint2*>(a.xq + dst * a.hidden + col) = codes;
-    if (lane16 == 0) a.xs[dst * kbs + kb] = s;
+    *reinterpret_cast<uint4*>(a.xq + dst * a.hidden + col) = codes;
+    if (ql == 0) a.xs[dst * kbs + kb] = s;
   }
 }
 
@@ -226,7 +232,7 @@ static void quant_grid(const StageArgs& a, int64_t* groups, int* blocks, int* co
     *blocks = (int)((*groups * 4 + 255) / 256);
   } else {
     *groups = (int64_t)a.tokens * (a.hidden / 128);
-    *blocks = (int)((*groups * 16 + 255) / 256);
+    *blocks = (int)((*groups * kQuantLanes + 255) / 256);
   }
   *copies = (a.flags & MOE_FLAG_PER_ROUTE_STAGING) ? a.top_k : 1;
 }
