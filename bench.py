@@ -149,12 +149,12 @@ def main():
     ap.add_argument("--expected-m", type=int, default=None,
                     help="expected rows per expert, which picks the token tile (default: T*K/E)")
     ap.add_argument("--sweep", default="", help="comma-separated token counts; extra lines to --sweep-out")
-    ap.add_argument("--sweep-out", default="gpurun_out/sweep.jsonl")
+    ap.add_argument("--sweep-out", default="bench_sweep.jsonl", help="file the sweep lines are appended to")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's share of the layer; runs on more than one GPU are not part of "
-              "this build (the expert-parallel exchange is out of scope).", file=sys.stderr)
+        print("bench.py measures one GPU's share of the layer; the library runs on one GPU, and the "
+              "expert-parallel exchange between GPUs is out of its scope.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
