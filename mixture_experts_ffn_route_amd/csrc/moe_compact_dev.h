@@ -250,7 +250,7 @@ __device__ __forceinline__ int32_t load_agent(int32_t* p) {
 // before the workgroup barrier, the arrival is an agent-scope atomic after
 // it, and the completing workgroup loads the counts at agent scope after its
 // atomic has returned.  No workgroup waits for another.
-__device__ inline void count_and_arrive(const CompactArgs& a, int blk, int* lds, const int* ids_lds,
+__device__ inline void count_and_arrive(const CompactArgs& a, int blk, int* lds, int* ids_lds,
                                         uint32_t status, int32_t tokens) {
   const int E = a.num_experts;
   int* hist = lds;                        // [waves, E]
@@ -274,33 +274,51 @@ __device__ inline void count_and_arrive(const CompactArgs& a, int blk, int* lds,
     scalar[2] = __hip_atomic_fetch_add(a.arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.blocks - 1;
   __syncthreads();
   if (!scalar[2]) return;
-  // The last arrival: header, then the scan over workgroups.  Each loop
-  // over workgroups loads 8 of them at once, so its round trips are
-  // blocks / 8, not blocks.
+  // The last arrival: header, then the scan over workgroups.  P threads
+  // share each expert (P = 256 / E for E <= 128, else 1), each over a
+  // contiguous range of workgroups, loading 8 of them per round trip; their
+  // partial sums get a per-expert prefix in LDS (with P = 1 the sum is the
+  // expert's total).  The threads of expert 0 also OR the workgroups' status
+  // bits.  LDS: the partial sums go to the ids area (E * P <= 256 ints, and
+  // a.chunk >= 1020) and the status word to the histogram, both free by now.
   constexpr int kBatch = 8;
-  if (threadIdx.x < 64) {
-    uint32_t v = 0;
-    if (threadIdx.x == kHdrStatus) {
-      for (int b0 = 0; b0 < a.blocks; b0 += kBatch) {
-        int32_t st[kBatch];
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j)
-          st[j] = b0 + j < a.blocks ? load_agent(reinterpret_cast<int32_t*>(a.blk_status) + b0 + j) : 0;
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) v |= (uint32_t)st[j];
-      }
-    }
-    if (threadIdx.x == kHdrTokens) v = (uint32_t)tokens;
-    a.hdr[threadIdx.x] = v;
-  }
-  for (int e = threadIdx.x; e < E; e += kCompactThreads) {
-    int run = 0;
-    for (int b0 = 0; b0 < a.blocks; b0 += kBatch) {
+  const int P = E <= kCompactThreads / 2 ? kCompactThreads / E : 1;
+  const int bp = (a.blocks + P - 1) / P;  // workgroups per part
+  int* part = ids_lds;                    // [E * P] when P > 1
+  uint32_t* status_or = reinterpret_cast<uint32_t*>(hist);
+  if (threadIdx.x == 0) *status_or = 0u;
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < E * P; idx += kCompactThreads) {
+    const int e = idx / P, b_lo = (idx - e * P) * bp, b_hi = min(b_lo + bp, a.blocks);
+    int sum = 0;
+    uint32_t st = 0;
+    for (int b0 = b_lo; b0 < b_hi; b0 += kBatch) {
       int c[kBatch];
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) c[j] = b0 + j < a.blocks ? load_agent(a.blk_base + (int64_t)(b0 + j) * E + e) : 0;
+      for (int j = 0; j < kBatch; ++j) c[j] = b0 + j < b_hi ? load_agent(a.blk_base + (int64_t)(b0 + j) * E + e) : 0;
+      if (e == 0) {
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) run += c[j];
+        for (int j = 0; j < kBatch; ++j)
+          st |= b0 + j < b_hi ? (uint32_t)load_agent(reinterpret_cast<int32_t*>(a.blk_status) + b0 + j) : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) sum += c[j];
+    }
+    if (P > 1)
+      part[idx] = sum;
+    else
+      cnt[e] = sum;
+    if (st) atomicOr(status_or, st);
+  }
+  __syncthreads();
+  if (threadIdx.x < 64)
+    a.hdr[threadIdx.x] = threadIdx.x == kHdrStatus ? *status_or : threadIdx.x == kHdrTokens ? (uint32_t)tokens : 0u;
+  for (int e = threadIdx.x; P > 1 && e < E; e += kCompactThreads) {  // totals; part[] becomes exclusive
+    int run = 0;
+    for (int p = 0; p < P; ++p) {
+      const int v = part[e * P + p];
+      part[e * P + p] = run;
+      run += v;
     }
     cnt[e] = run;
   }
@@ -309,15 +327,16 @@ __device__ inline void count_and_arrive(const CompactArgs& a, int blk, int* lds,
   __syncthreads();
   // each workgroup's first position per expert: the expert's offset plus the
   // counts of the workgroups before it
-  for (int e = threadIdx.x; e < E; e += kCompactThreads) {
-    int run = tmp[e];
-    for (int b0 = 0; b0 < a.blocks; b0 += kBatch) {
+  for (int idx = threadIdx.x; idx < E * P; idx += kCompactThreads) {
+    const int e = idx / P, b_lo = (idx - e * P) * bp, b_hi = min(b_lo + bp, a.blocks);
+    int run = tmp[e] + (P > 1 ? part[idx] : 0);
+    for (int b0 = b_lo; b0 < b_hi; b0 += kBatch) {
       int c[kBatch];
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) c[j] = b0 + j < a.blocks ? load_agent(a.blk_base + (int64_t)(b0 + j) * E + e) : 0;
+      for (int j = 0; j < kBatch; ++j) c[j] = b0 + j < b_hi ? load_agent(a.blk_base + (int64_t)(b0 + j) * E + e) : 0;
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
-        if (b0 + j < a.blocks) a.blk_base[(int64_t)(b0 + j) * E + e] = run;
+        if (b0 + j < b_hi) a.blk_base[(int64_t)(b0 + j) * E + e] = run;
         run += c[j];
       }
     }
