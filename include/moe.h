@@ -34,7 +34,10 @@
  *    is bounded; one that gives up sets MOE_DEV_WAIT_TIMEOUT instead of
  *    hanging.
  *  - Calls on one layer handle are not thread-safe; distinct handles with
- *    distinct workspaces are independent.
+ *    distinct workspaces are independent.  The launches of one handle must
+ *    also not overlap on the device (issue them on one stream, or order the
+ *    streams): its workspace holds the staged batch between calls and a
+ *    counter the staging launch leaves at zero for the next one.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
