@@ -132,6 +132,27 @@ def test_multi_workgroup_compaction_repeated():
         assert_output_close(_bits(out), res.out_bits, f"T={T}")
 
 
+def test_stage_codes_at_tiny_magnitudes():
+    """The quantiser forms x / s from a reciprocal with one correction step
+    for blocks with s >= 2^-90 and divides below that.  Rows scaled across
+    that bound, and down to subnormal bf16, stage bit for bit as the oracle's
+    IEEE quotient."""
+    from oracle.formats import bf16_bits_to_f64, bf16_rne_bits
+    shape = CONFIGS["small"]
+    inp = make_layer_inputs(shape, seed=43)
+    x = bf16_bits_to_f64(inp.x_bf16)
+    scales = [1e-26, 3e-26, 1e-25, 4e-25, 1e-22, 1e-30, 1e-36, 1e-38, 3e-39]
+    for i, f in enumerate(scales):
+        x[i::len(scales) + 3] *= f  # a spread of rows at each magnitude, the rest as drawn
+    inp.x_bf16 = bf16_rne_bits(x)
+    layer, dev, out = _gpu_run(inp, shape)
+    res = M.forward_fp8(inp.x_bf16, inp.topk_idx, inp.topk_w, inp.w13, inp.w13_scale, inp.w2, inp.w2_scale)
+    amax = np.abs(bf16_bits_to_f64(inp.x_bf16)).reshape(shape.tokens, -1, 128).max(axis=2)
+    s = (amax / 448.0).astype(np.float32)
+    assert np.any((s > 0) & (s < 2.0 ** -90)) and np.any((s >= 2.0 ** -90) & (s < 2.0 ** -80))
+    _check_stage(layer, res, shape, shape.tokens)
+
+
 @pytest.mark.parametrize("pair", [(8, 48), (2, 24), (96, 4096), (128, 200), (8, 4096)])
 def test_tactics_agree_bit_exact(pair):
     """Every token tile (16 to 256 tokens) computes the same bits: each
