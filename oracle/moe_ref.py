@@ -68,26 +68,66 @@ STATUS_NONFINITE = 4
 STATUS_CAPACITY = 8
 
 PIN_STATUS = {
-    "formats.e4m3_decode": "pinned: exhaustive vs OCP bit-field values and torch.float8_e4m3fn",
-    "formats.e5m2_decode": "pinned: exhaustive vs OCP bit-field values and torch.float8_e5m2",
-    "formats.bf16_bits_to_f64": "pinned: round trips of the bfloat16 rounding tests (exact widening)",
-    "formats.e8m0_decode": "pinned: exhaustive vs torch.float8_e8m0fnu",
-    "formats.e4m3_encode_rne_sat": "pinned: all midpoints +-1 ulp and random values vs torch cast",
-    "formats.bf16_rne_bits": "pinned: vs torch bfloat16 cast (float32 inputs) and exact fractions",
-    "dequant_block128": "pinned: exact-rational FC1 and one-hot FC1/FC2 closed forms recompute it",
-    "dequant_rows_1x128": "pinned: exact-rational FC1 recomputes it from the codes and scales",
-    "dequant_mx": "pinned: one-hot MX closed form and the per-route loop recompute 2^(e-127) scaling",
-    "silu": "pinned: one-hot SwiGLU closed form g/(1+exp(-g))*u",
-    "requant_1x128": "pinned: requantisation invariants (scale = amax/448, a code at 448, error bound)",
-    "fc1_gateup": "pinned: exact rational (fractions) on the tiny shape, one-hot closed form",
-    "stage_quantize_1x128": "pinned: torch-cast cross-check, amax->448 invariant, error bound",
-    "stage_routes": "pinned: brute-force loops and masked-route semantics",
-    "compact": "pinned: brute-force loops",
-    "fc1_swiglu_requant": "pinned: exact rational FC1, one-hot closed forms, requant invariants",
-    "fc2": "pinned: brute-force loops, one-hot closed form",
-    "combine": "pinned: K=1 identity, power-of-two scaling, all-masked token, masked NaN",
-    "forward_fp8": "pinned: pure-Python per-route loop on tiny shapes; dedup == per-route",
-    "forward_mx": "pinned: one-hot closed forms and pure-Python loop on tiny shapes",
+    # value: "pinned: <what fixes it> [<test module>::<test>, ...]"; the tests
+    # named in brackets must exist (checked by test_every_oracle_function_has_a_pin)
+    "formats.e4m3_decode": "pinned: exhaustive vs OCP bit-field values and torch.float8_e4m3fn "
+                           "[test_oracle_formats::test_e4m3_decode_exhaustive_vs_torch, "
+                           "test_oracle_formats::test_e4m3_decode_spec_values]",
+    "formats.e5m2_decode": "pinned: exhaustive vs OCP bit-field values and torch.float8_e5m2 "
+                           "[test_oracle_formats::test_e5m2_decode_exhaustive_vs_torch, "
+                           "test_oracle_formats::test_e5m2_decode_spec_values]",
+    "formats.bf16_bits_to_f64": "pinned: round trips of the bfloat16 rounding tests (exact widening) "
+                                "[test_oracle_formats::test_bf16_rne_float32_inputs_vs_torch]",
+    "formats.e8m0_decode": "pinned: exhaustive vs torch.float8_e8m0fnu "
+                           "[test_oracle_formats::test_e8m0_decode_exhaustive_vs_torch]",
+    "formats.e4m3_encode_rne_sat": "pinned: all midpoints +-1 ulp and random values vs torch cast "
+                                   "[test_oracle_formats::test_e4m3_encode_midpoints_vs_torch, "
+                                   "test_oracle_formats::test_e4m3_encode_float64_near_midpoints_vs_exact]",
+    "formats.bf16_rne_bits": "pinned: vs torch bfloat16 cast (float32 inputs) and exact fractions "
+                             "[test_oracle_formats::test_bf16_rne_float32_inputs_vs_torch, "
+                             "test_oracle_formats::test_bf16_rne_float64_single_rounding]",
+    "dequant_block128": "pinned: exact-rational FC1 and one-hot FC1/FC2 closed forms recompute it "
+                        "[test_oracle_layer::test_fc1_exact_rational_tiny, test_oracle_layer::test_fc2_one_hot_closed_form]",
+    "dequant_rows_1x128": "pinned: exact-rational FC1 recomputes it from the codes and scales "
+                          "[test_oracle_layer::test_fc1_exact_rational_tiny]",
+    "dequant_mx": "pinned: one-hot MX closed forms and per-route loops, e4m3 and e5m2 elements "
+                  "[test_oracle_layer::test_forward_mx_one_hot_and_loop, "
+                  "test_oracle_branches::test_forward_mx_e5m2_one_hot, "
+                  "test_oracle_branches::test_mx_e5m2_pins_catch_element_type_mistakes]",
+    "silu": "pinned: one-hot SwiGLU closed form g/(1+exp(-g))*u "
+            "[test_oracle_layer::test_fc1_swiglu_one_hot_closed_form]",
+    "requant_1x128": "pinned: requantisation invariants (scale = amax/448, a code at 448, error bound) "
+                     "[test_oracle_layer::test_fc1_swiglu_one_hot_closed_form]",
+    "fc1_gateup": "pinned: exact rational (fractions) on the tiny shape, one-hot closed form "
+                  "[test_oracle_layer::test_fc1_exact_rational_tiny, test_oracle_layer::test_fc2_and_fc1_brute_force_loops]",
+    "stage_quantize_1x128": "pinned: torch-cast cross-check, amax->448 invariant, error bound "
+                            "[test_oracle_stage_compact::test_stage_quant_matches_torch_cast_and_invariants]",
+    "stage_routes": "pinned: brute-force loops and masked-route semantics "
+                    "[test_oracle_stage_compact::test_stage_routes_vs_brute_force, "
+                    "test_oracle_stage_compact::test_masked_routes_accept_nonfinite_weights]",
+    "compact": "pinned: brute-force loops [test_oracle_stage_compact::test_compact_vs_brute_force, "
+               "test_oracle_stage_compact::test_compact_capacity_drops_tail_in_sorted_order]",
+    "fc1_swiglu_requant": "pinned: exact rational FC1, one-hot closed forms, requant invariants "
+                          "[test_oracle_layer::test_fc1_swiglu_one_hot_closed_form]",
+    "fc1_swiglu_requant[bf16_gateup=True]": "pinned: one-hot closed form requant(silu(bf16(g)) * bf16(u)), "
+                                            "misplaced rounding caught "
+                                            "[test_oracle_branches::test_forward_fp8_bf16_gateup_one_hot, "
+                                            "test_oracle_branches::test_bf16_gateup_pin_catches_misplaced_rounding]",
+    "fc2": "pinned: brute-force loops, one-hot closed form "
+           "[test_oracle_layer::test_fc2_and_fc1_brute_force_loops, test_oracle_layer::test_fc2_one_hot_closed_form]",
+    "combine": "pinned: K=1 identity, power-of-two scaling, all-masked token, masked NaN "
+               "[test_oracle_layer::test_combine_identities, test_oracle_layer::test_masked_nan_weights_do_not_change_output]",
+    "forward_fp8": "pinned: pure-Python per-route loop on tiny shapes; dedup == per-route "
+                   "[test_oracle_layer::test_forward_fp8_vs_per_route_loop, test_oracle_layer::test_dedup_equals_per_route_staging]",
+    "forward_fp8[bf16_gateup=True]": "pinned: one-hot closed form through the whole layer "
+                                     "[test_oracle_branches::test_forward_fp8_bf16_gateup_one_hot]",
+    "forward_mx": "pinned: one-hot closed forms and pure-Python loop on tiny shapes "
+                  "[test_oracle_layer::test_forward_mx_one_hot_and_loop]",
+    "forward_mx[elem=e5m2]": "pinned: one-hot e5m2 W13/W2 closed forms with bit-field decode, per-route loop, "
+                             "element-type mistakes caught "
+                             "[test_oracle_branches::test_forward_mx_e5m2_one_hot, "
+                             "test_oracle_branches::test_forward_mx_e5m2_per_route_loop, "
+                             "test_oracle_branches::test_mx_e5m2_pins_catch_element_type_mistakes]",
 }
 
 

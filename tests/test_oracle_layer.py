@@ -262,14 +262,25 @@ def test_page_figure_fused_fc1_buffer():
 
 
 def test_every_oracle_function_has_a_pin():
-    """Every public function of the oracle names the pin that holds it."""
+    """Every public function of the oracle (and each optional branch that a
+    GPU path is compared with) names the tests that pin it, and those tests
+    exist."""
+    import importlib
     import inspect
+    import re
 
     from oracle import formats as OF
     for mod, prefix in ((M, ""), (OF, "formats.")):
         for name, fn in inspect.getmembers(mod, inspect.isfunction):
             if name.startswith("_") or fn.__module__ != mod.__name__:
                 continue
-            key = prefix + name
-            assert key in M.PIN_STATUS, f"{key} has no PIN_STATUS entry"
-            assert M.PIN_STATUS[key].startswith("pinned:"), key
+            assert prefix + name in M.PIN_STATUS, f"{prefix + name} has no PIN_STATUS entry"
+    for branch in ("forward_mx[elem=e5m2]", "forward_fp8[bf16_gateup=True]", "fc1_swiglu_requant[bf16_gateup=True]"):
+        assert branch in M.PIN_STATUS, branch
+    for key, text in M.PIN_STATUS.items():
+        assert text.startswith("pinned:"), key
+        refs = re.findall(r"(test_\w+)::(test_\w+)", text)
+        assert refs, f"{key} names no pinning test"
+        for module, test in refs:
+            mod = importlib.import_module(f"tests.{module}")
+            assert callable(getattr(mod, test, None)), f"{key}: {module}::{test} does not exist"
