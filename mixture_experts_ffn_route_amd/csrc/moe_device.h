@@ -84,8 +84,63 @@ __device__ __forceinline__ float swiglu(float g, float u) {
 
 // 1x128 requantisation factor: codes are RNE_sat(h * inv) with
 // inv = 448 / amax, and 0 when the block's scale s = amax / 448 is 0.
+// `amax` must be at least 2^-64 (see requant_prescale), so that the
+// reciprocal cannot overflow.
 __device__ __forceinline__ float requant_inv(float amax, float s) {
   return s != 0.f ? kE4m3Max * __builtin_amdgcn_rcpf(amax) : 0.f;
+}
+
+// A block whose amax lies below 2^-64 (down to FP32 subnormals, where
+// 1 / amax overflows) is requantised from h * 2^64 and amax * 2^64: both
+// products are exact, and the codes of (h * 2^64) * 448 / (amax * 2^64) are
+// those of h * 448 / amax.  Returns the factor to apply to h (1 or 2^64).
+__device__ __forceinline__ float requant_prescale(float& amax) {
+  const float f = amax < 0x1p-64f ? 0x1p64f : 1.0f;
+  amax *= f;
+  return f;
+}
+
+// Block-scale promotion of the FP8 GEMMs.  An output accumulates
+// sum_kb F_kb * P_kb over K-blocks, with F_kb = sx * sw the product of the
+// activation and weight block scales and P_kb the K-block's FP8 code product.
+// The accumulator is kept in units of m * 2^ref, where m in [1/4, 1) is the
+// mantissa product of the current block's two scales and ref the largest
+// exponent sum seen so far; the MFMA applies each block's own 2^(e - ref)
+// as its E8M0 operand scale (exact), and before a block's MFMA the
+// accumulator is multiplied by
+//   r = (m_prev / m) * 2^(ref_prev - ref)      (|r| < 4)
+// so no ratio of scales, however far apart, overflows or is lost.  After the
+// last block, out = ldexp(acc * m_last, ref).  A block whose scale is zero
+// contributes nothing (its products enter at 2^-127 of the current unit, or
+// are discarded with r = 0 when no block with a nonzero scale preceded it);
+// with no such block at all the output is 0.
+struct Promo {
+  float m;  // mantissa product of the last nonzero block, 0 while none
+  int e;    // ref: largest exponent sum so far
+};
+
+// One K-block: returns the accumulator ratio r and sets `sh` to the E8M0
+// byte (127 + e - ref, at least 0) of the block's MFMA.
+__device__ __forceinline__ float promo_step(float sx, float sw, Promo& p, int& sh) {
+  const float m = __builtin_amdgcn_frexp_mantf(sx) * __builtin_amdgcn_frexp_mantf(sw);
+  const int e = __builtin_amdgcn_frexp_expf(sx) + __builtin_amdgcn_frexp_expf(sw);
+  float r;
+  if (m == 0.f) {
+    r = 1.f;
+    sh = 0;
+  } else if (p.m == 0.f) {
+    r = 0.f;
+    p.m = m;
+    p.e = e;
+    sh = 127;
+  } else {
+    const int ref = max(p.e, e);
+    r = __builtin_amdgcn_ldexpf(p.m * __builtin_amdgcn_rcpf(m), p.e - ref);
+    p.m = m;
+    p.e = ref;
+    sh = max(127 + e - ref, 0);
+  }
+  return r;
 }
 
 // Maximum over groups of `width` consecutive lanes (width a power of two <= 64).

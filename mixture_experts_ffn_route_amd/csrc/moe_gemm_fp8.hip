@@ -12,11 +12,13 @@
 // Limitations.
 //
 // Design (CDNA4):
-//  * One K-block of 128 is exactly one v_mfma_f32_16x16x128_f8f6f4.  The
-//    block scales are applied by keeping the accumulator divided by the
-//    current block's scale product (see carry_scale): one multiply per output
-//    per K-block rescales it and the MFMA accumulates in place, so no MFMA
-//    result needs registers of its own.
+//  * One K-block of 128 is exactly one 16x16x128 f8f6f4 MFMA.  The block
+//    scales are applied by keeping the accumulator in units of the current
+//    block's scale product (promo_step in moe_device.h): the MFMA's E8M0
+//    operand scale applies the product's power-of-two part exactly, one
+//    multiply per output per K-block applies the mantissa ratio, and the
+//    MFMA accumulates in place, so no MFMA result needs registers of its
+//    own.
 //  * Weights are the MFMA row operand and tokens the column operand, so a
 //    lane's four outputs of a 16x16 block share one token and one weight
 //    block: one scale product per lane per token block.
@@ -64,18 +66,14 @@ constexpr int kMaxKBlocks = 128;  // K <= 16384
 constexpr int kWsBytes = 2 * kMaxKBlocks * 4;  // per-tile weight-scale columns
 constexpr int kRingBytes = kLdsBytes - kWsBytes;
 
-__device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
-
-// Scale product of one K-block for the promotion recursion.  The accumulator
-// is kept divided by the current block's product F = sx * sw:
-//   acc_kb = acc_{kb-1} * (F_{kb-1} / F_kb) + sum_k a*b     (MFMA with C input)
-// and multiplied by the last F after the K loop, which equals
-// sum_kb F_kb * sum_k a*b.  A block whose F is zero or subnormal carries the
-// previous F (its product is zero: its codes are all zero).
-__device__ __forceinline__ float carry_scale(float f, float prev) {
-  return fabsf(f) >= 0x1p-100f ? f : prev;
+// One 16x16x128 e4m3 MFMA whose products are scaled by 2^(byte - 127),
+// `byte` taken from byte OB of the token operand's scale word (lane l
+// supplies it for token l % 16; every lane of a token holds the same word),
+// the weight operand at 2^0.  This is the block-scale promotion's exact
+// power-of-two part (promo_step in moe_device.h).
+template <int OB>
+__device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, OB, sb);
 }
 
 // LDS is addressed through 32-bit address-space-3 pointers throughout: no
@@ -225,8 +223,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring3[C::STAGES > 3 ? C::STAGE : 16];
   __shared__ __attribute__((aligned(16))) float wsc[2 * kMaxKBlocks];  // weight scales [block 0 | block 1][kb]
   __shared__ __attribute__((aligned(16))) float sx0[BT];               // token scales of K-block 0
-  __shared__ __attribute__((aligned(16))) float rsc[2][BT][2];          // promotion ratios, double-buffered
-  __shared__ __attribute__((aligned(16))) float fsc[BT][2];             // final scale products
+  __shared__ __attribute__((aligned(16))) float rsc[2][BT][4];          // promotion records, double-buffered
+  __shared__ __attribute__((aligned(16))) float fsc[BT][4];             // final scales (m0, m1, e0, e1)
   __shared__ __attribute__((aligned(16))) uint32_t l2sink[kThreads];    // L2 prefetch landing words (never read)
   __shared__ __attribute__((aligned(16))) float red_s[FC1 ? C::WN * BT : 4];  // FC1 epilogue: partial amax
   __shared__ int32_t cb_list[FC1 ? 1 : BT];  // FC2 fused combine: tokens this tile completes
@@ -258,8 +256,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_persist_kernel(GemmArgs 
   __shared__ __attribute__((aligned(1024))) uint8_t ring3[C::STAGES > 3 ? C::STAGE : 16];
   __shared__ __attribute__((aligned(16))) float wsc[2 * kMaxKBlocks];
   __shared__ __attribute__((aligned(16))) float sx0[BT];
-  __shared__ __attribute__((aligned(16))) float rsc[2][BT][2];
-  __shared__ __attribute__((aligned(16))) float fsc[BT][2];
+  __shared__ __attribute__((aligned(16))) float rsc[2][BT][4];
+  __shared__ __attribute__((aligned(16))) float fsc[BT][4];
   __shared__ __attribute__((aligned(16))) uint32_t l2sink[kThreads];
   __shared__ __attribute__((aligned(16))) float red_s[C::WN * BT];
   __shared__ int32_t cb_list[BT];

@@ -47,17 +47,19 @@ __device__ inline void quant_1x128(const StageArgs& a, int64_t g, int64_t groups
     } else {
       // x / s without an IEEE division per element: inv = fl32(1/s) once,
       // then q0 = fl32(x * inv), r = fma(-q0, s, x) and q = fma(r, inv, q0)
-      // (a reciprocal with one correction step).  For every bf16 x with
-      // |x| <= amax and every block with s >= 2^-90 this gives the e4m3 code
-      // of the IEEE quotient, checked exhaustively; below that (amax under
-      // ~3.6e-25) the remainder can underflow, so such blocks divide.
+      // (a reciprocal with one correction step), given the sign of x (the
+      // sums give +0 for x = -0, whose quotient is -0, code 0x80).  For every
+      // bf16 x with |x| <= amax and every block with s >= 2^-90 this gives
+      // the e4m3 code of the IEEE quotient, checked exhaustively; below that
+      // (amax under ~3.6e-25) the remainder can underflow, so such blocks
+      // divide.
       float q[16];
       if (s >= 0x1p-90f) {
         const float inv = 1.0f / s;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float q0 = v[i] * inv;
-          q[i] = fmaf(fmaf(-q0, s, v[i]), inv, q0);
+          q[i] = copysignf(fmaf(fmaf(-q0, s, v[i]), inv, q0), v[i]);
         }
       } else {
 #pragma unroll

@@ -37,9 +37,14 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(const float* gateup, 
   float m = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(h[i]));
-  const float amax = group_max<16>(m);
+  float amax = group_max<16>(m);
   const float s = amax / kE4m3Max;
+  const float pre = requant_prescale(amax);
   const float inv = requant_inv(amax, s);
+  if (pre != 1.0f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] *= pre;
+  }
   int w0 = cvt2_e4m3(h[0] * inv, h[1] * inv, 0, false);
   w0 = cvt2_e4m3(h[2] * inv, h[3] * inv, w0, true);
   int w1 = cvt2_e4m3(h[4] * inv, h[5] * inv, 0, false);

@@ -250,3 +250,32 @@ def test_mx_e5m2_dsv3_sampled():
     assert layer.status() == 0
     _check_compaction(layer, res, shape, shape.tokens)
     assert_output_close(_bits(out)[tok], res.out_bits, "mx e5m2 dsv3 T=4096")
+
+
+@pytest.mark.slow
+def test_mx_dsv3_small_token_counts_sampled():
+    """MXFP8 x BF16 at the DSV3-like shape (H=7168) for decode and mid token
+    counts, each in the benchmark's launch configuration: T=8 and 64
+    (16-token tiles) and T=512 (128-token tiles).  A token's output depends
+    only on its own routes, so one oracle call over tokens sampled from the
+    first 8, 64 and 512 serves the three layers."""
+    base = CONFIGS["dsv3"]
+    shape = MoEShape(512, base.hidden, base.intermediate, base.experts, base.top_k, base.routing)
+    inp = _mx_inputs(shape, 6)
+    dev = to_device(inp)
+    rng = np.random.default_rng(6)
+    tok = np.concatenate([np.arange(8), np.sort(rng.choice(np.arange(8, 64), 8, replace=False)),
+                          np.sort(rng.choice(np.arange(64, 512), 8, replace=False))])
+    res = _oracle(inp, token_ids=tok)
+    for T, block_m in [(8, 16), (64, 16), (512, 128)]:
+        sub = MoEShape(T, base.hidden, base.intermediate, base.experts, base.top_k, base.routing)
+        layer = make_layer(sub, dev, mx="e4m3")
+        assert layer.tactic()["block_m"] == block_m
+        out = run_forward(layer, dev, tokens=T)
+        torch.cuda.synchronize()
+        assert layer.status() == 0
+        sel = tok < T
+        assert_output_close(_bits(out)[tok[sel]], res.out_bits[sel], f"mx dsv3 T={T}")
+        if T == shape.tokens:
+            _check_compaction(layer, res, shape, T)
+        del layer, out

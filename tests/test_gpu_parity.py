@@ -151,6 +151,51 @@ def test_stage_codes_at_tiny_magnitudes():
     s = (amax / 448.0).astype(np.float32)
     assert np.any((s > 0) & (s < 2.0 ** -90)) and np.any((s >= 2.0 ** -90) & (s < 2.0 ** -80))
     _check_stage(layer, res, shape, shape.tokens)
+    # the layer output of those rows: every block-scale product of the tiny
+    # rows lies far below 2^-100 (their outputs are +0 or subnormal)
+    _check_compaction(layer, res, shape, shape.tokens)
+    assert_output_close(_bits(out), res.out_bits, "tiny magnitudes")
+
+
+@pytest.mark.parametrize("expected_m", [None, 16, 4096])
+def test_block_scales_across_the_float32_range(expected_m):
+    """Block scales that differ by up to 2^120 within one output's sum, for
+    both GEMMs, against the oracle.
+
+    FC1: activation rows whose 1x128 blocks are scaled by 2^-40..2^20, rows
+    with one block 2^-80 below the others (a scale product near 2^-100),
+    rows with zero blocks and whole rows at 1e-26 (every product below
+    2^-100).  FC2: the W13 block scales of some 128-column blocks of h are
+    divided by 2^60 or 2^70, so those h blocks sit 2^120 to 2^140 below the
+    rest of their row (h scales near or below the float32 normal range).
+    Checked at the 16-, 128- and 256-token tiles."""
+    from oracle.formats import bf16_bits_to_f64, bf16_rne_bits
+    shape = CONFIGS["small"]
+    T, H = shape.tokens, shape.hidden
+    inp = make_layer_inputs(shape, seed=47)
+    rng = np.random.default_rng(47)
+    x = bf16_bits_to_f64(inp.x_bf16).reshape(T, H // 128, 128)
+    x[0::5] *= np.exp2(rng.integers(-40, 21, (len(range(0, T, 5)), H // 128, 1)))
+    x[1::5, 7] *= 2.0 ** -80
+    x[2::5, ::3] = 0.0
+    x[3::10] *= 1e-26
+    inp.x_bf16 = bf16_rne_bits(x.reshape(T, H))
+    s13 = inp.w13_scale.copy()
+    ib = shape.intermediate // 128
+    s13[:, 1, :] *= np.float32(2.0 ** -60)            # gate rows of h block 1
+    s13[:, ib + 1, :] *= np.float32(2.0 ** -60)       # up rows of h block 1
+    s13[:, 4, :] *= np.float32(2.0 ** -70)
+    s13[:, ib + 4, :] *= np.float32(2.0 ** -70)
+    inp.w13_scale = s13
+    layer, dev, out = _gpu_run(inp, shape, expected_m=expected_m)
+    res = M.forward_fp8(inp.x_bf16, inp.topk_idx, inp.topk_w, inp.w13, inp.w13_scale, inp.w2, inp.w2_scale)
+    assert layer.status() == 0
+    _check_stage(layer, res, shape, T)
+    assert_output_close(_bits(out), res.out_bits, f"wide block-scale range, expected_m={expected_m}")
+    # the h blocks scaled down carry scales 2^120+ below their neighbours
+    hs = np.stack([res.hs[p] for p in range(int(res.comp.offsets[-1]))])
+    live = hs[:, 0] > 0
+    assert np.all(hs[live, 1] < hs[live, 0] * 2.0 ** -100)
 
 
 @pytest.mark.parametrize("pair", [(8, 48), (2, 24), (96, 4096), (128, 200), (8, 4096)])
@@ -264,6 +309,18 @@ def _sampled_full_size(shape, seed, n_sample, label):
 @pytest.mark.slow
 def test_dsv3_shape_sampled():
     _sampled_full_size(CONFIGS["dsv3"], 0, 24, "dsv3 T=4096")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("tokens", [512, 32768])
+def test_dsv3_sweep_points_sampled(tokens):
+    """Token-sweep points of the DSV3-like shape in the benchmark's launch
+    configuration: T=512 (128-token tiles, 56 K-blocks, one compaction
+    workgroup for each 1024 routes: four) and T=32768 (256-token tiles, 256
+    compaction workgroups, 262144 route rows, 3.76 GB of FC2 rows)."""
+    base = CONFIGS["dsv3"]
+    shape = MoEShape(tokens, base.hidden, base.intermediate, base.experts, base.top_k, base.routing)
+    _sampled_full_size(shape, 3, 16, f"dsv3 T={tokens}")
 
 
 @pytest.mark.slow

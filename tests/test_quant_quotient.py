@@ -44,10 +44,12 @@ def _rn32(v: Fraction) -> np.float32:
     return np.float32((1 if v > 0 else -1) * float(n * ulp))
 
 
-def _quotients(x: np.ndarray, s: np.float32) -> np.ndarray:
-    """The kernel's float32 quotients of x by s (s >= S_MIN)."""
+def _quotients(x: np.ndarray, s: np.float32, sign_fix: bool = True) -> np.ndarray:
+    """The kernel's float32 quotients of x by s (s >= S_MIN), given the sign
+    of x (the sums alone turn x = -0 into +0)."""
     inv = np.float32(1.0) / s
-    q0 = x * inv
+    with np.errstate(invalid="ignore"):
+        q0 = x * inv
     r = (x.astype(np.float64) - q0.astype(np.float64) * np.float64(s)).astype(np.float32)
     t = q0.astype(np.float64) + r.astype(np.float64) * np.float64(inv)
     q = t.astype(np.float32)
@@ -55,7 +57,7 @@ def _quotients(x: np.ndarray, s: np.float32) -> np.ndarray:
     tie = (back != t) & (np.abs(t - back) == np.spacing(np.abs(q)).astype(np.float64) / 2)
     for i in np.nonzero(tie)[0]:
         q[i] = _rn32(Fraction(float(q0[i])) + Fraction(float(r[i])) * Fraction(float(inv)))
-    return q
+    return np.copysign(q, x) if sign_fix else q
 
 
 def test_division_free_quotient_gives_the_ieee_codes():
@@ -75,7 +77,8 @@ def test_division_free_quotient_gives_the_ieee_codes():
         x = xall[:np.searchsorted(xabs, amax, side="right")]
         want = x / s  # IEEE float32 division
         got = _quotients(x, s)
-        diff = want != got
+        # -0 == +0 in float comparison: the sign bits are compared too
+        diff = (want != got) | (np.signbit(want) != np.signbit(got))
         if diff.any():
             wc = e4m3_encode_rne_sat(want[diff].astype(np.float64))
             gc = e4m3_encode_rne_sat(got[diff].astype(np.float64))
@@ -99,3 +102,13 @@ def test_a_plausible_mistake_is_caught():
             found = True
             break
     assert found
+
+
+def test_negative_zero_keeps_its_code():
+    """x = -0 must give code 0x80 (the IEEE quotient is -0); the correction
+    sums alone give +0 (code 0x00)."""
+    x = np.array([-0.0, 0.0, -1.0, 1.0], np.float32)
+    s = np.float32(np.float32(1.0) / np.float32(448.0))
+    assert list(e4m3_encode_rne_sat(_quotients(x, s).astype(np.float64))[:2]) == [0x80, 0x00]
+    assert list(e4m3_encode_rne_sat((x / s).astype(np.float64))[:2]) == [0x80, 0x00]
+    assert e4m3_encode_rne_sat(_quotients(x, s, sign_fix=False).astype(np.float64))[0] == 0x00
