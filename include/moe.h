@@ -268,6 +268,29 @@ moe_status_t moe_stage_inputs(moe_layer_t* layer, const void* x, const float* x_
  * host-side synchronization in the steady-state forward). */
 moe_status_t moe_layer_forward(moe_layer_t* layer, void* stream);
 
+/* Stage + forward of one batch without allocating: for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid it).  Same arguments and results as
+ * moe_stage_inputs followed by moe_layer_forward, on the same kernels, except
+ * that every per-call region (staged rows and routes, compaction, FC1
+ * output, FC2 rows, tile list, status header) lives in a static device
+ * scratch of 64 MiB per device that the library holds until the process
+ * ends; the layer's workspace supplies only its create-time weight tiles
+ * and is not written.
+ *  status_bits  device uint32, may be NULL: receives the call's MOE_DEV_*
+ *               bits (moe_read_status does not see them).
+ * The handle's own staged batch (moe_stage_inputs) is left as it was.
+ * MOE_ERR_CAPACITY when num_tokens > max_rows or when the call's regions do
+ * not fit in the scratch (about 139 KB per token at H=7168, I=2048, K=8:
+ * some 480 tokens); nothing is launched then.  Calls no hipMalloc, hipFree
+ * or allocating routine (the first call on a device looks up the scratch's
+ * address).  Every call on a device shares that device's scratch, and it
+ * keeps the last call's contents: calls that overlap on one device (on
+ * different streams, or from different threads) race. */
+moe_status_t moe_layer_forward_noalloc(moe_layer_t* layer, const void* x, const float* x_scale,
+                                       const int32_t* topk_idx, const float* topk_w, int32_t num_tokens,
+                                       void* out_bf16, uint32_t* status_bits, void* stream);
+
 /* Synchronise `stream` and return the device status bits (MOE_DEV_*)
  * accumulated since the last moe_stage_inputs.  bits: [host out]. */
 moe_status_t moe_read_status(moe_layer_t* layer, void* stream, uint32_t* bits);

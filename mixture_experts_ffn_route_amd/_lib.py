@@ -52,7 +52,7 @@ PROFILE_ALL = (1 << len(KERNELS)) - 1
 # Every symbol include/moe.h declares.
 EXPORTS = (
     "moe_workspace_query", "moe_layer_create", "moe_stage_inputs", "moe_layer_forward",
-    "moe_read_status", "moe_layer_region", "moe_layer_tactic", "moe_profile_enable",
+    "moe_layer_forward_noalloc", "moe_read_status", "moe_layer_region", "moe_layer_tactic", "moe_profile_enable",
     "moe_profile_read", "moe_layer_destroy", "moe_token_bucket", "moe_status_string",
     "moe_last_error",
 )
@@ -103,6 +103,7 @@ def _load() -> ctypes.CDLL:
                                    vp, POINTER(vp)]),
         "moe_stage_inputs": (i32, [vp, vp, vp, vp, vp, i32, vp, vp]),
         "moe_layer_forward": (i32, [vp, vp]),
+        "moe_layer_forward_noalloc": (i32, [vp, vp, vp, vp, vp, i32, vp, vp, vp]),
         "moe_read_status": (i32, [vp, vp, POINTER(c_uint32)]),
         "moe_layer_region": (i32, [vp, i32, POINTER(vp), POINTER(c_size_t)]),
         "moe_layer_tactic": (i32, [vp, POINTER(moe_tactic_t)]),
@@ -169,6 +170,12 @@ def moe_stage_inputs(layer: int, x: int, x_scale: int, topk_idx: int, topk_w: in
 
 def moe_layer_forward(layer: int, stream: int = 0) -> None:
     _check(_lib.moe_layer_forward(layer, stream))
+
+
+def moe_layer_forward_noalloc(layer: int, x: int, x_scale: int, topk_idx: int, topk_w: int, num_tokens: int,
+                              out_bf16: int, status_bits: int = 0, stream: int = 0) -> None:
+    _check(_lib.moe_layer_forward_noalloc(layer, x, x_scale or None, topk_idx, topk_w, num_tokens, out_bf16,
+                                          status_bits or None, stream))
 
 
 def moe_read_status(layer: int, stream: int = 0) -> int:

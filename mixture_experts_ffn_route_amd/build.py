@@ -1,6 +1,6 @@
 """Ahead-of-time build of the gfx950 HIP library ``libmoe_mi355x.so`` (in-tree).
 
-``python -m mixture_experts_ffn_route_amd.build`` compiles every source under
+``python mixture_experts_ffn_route_amd/build.py`` compiles every source under
 ``csrc/`` with hipcc for gfx950 and links the shared library next to this
 file.  Objects go to ``_build/`` at the repository root.
 """
@@ -32,6 +32,7 @@ SOURCES = [
     "moe_swiglu.hip",
     "moe_combine.hip",
     "moe_weights.hip",
+    "moe_noalloc.hip",
 ]
 
 # Packed FP32 VALU ops are disabled for all device code.

@@ -34,6 +34,12 @@ struct moe_layer {
   int32_t grid_persist;  // MOE_FLAG_PERSISTENT_FFN: cooperative grid of the FC1->FC2 launch
   // profiling: event pairs around the launches of the classes in prof_mask
   uint32_t prof_mask;
+  // Where the per-call regions (everything but the create-time weight tiles)
+  // live: the workspace, or the static scratch during
+  // moe_layer_forward_noalloc.
+  uint8_t* cur_base;
+  const moe::Layout* cur_L;
+  int32_t cur_max_rows;
   std::vector<EventPair> pending;
   std::vector<hipEvent_t> pool;
   double ms[MOE_KERNEL_COUNT];
@@ -42,9 +48,16 @@ struct moe_layer {
 
 namespace {
 
+bool is_weight_region(int r) {
+  return r == MOE_REGION_W13T || r == MOE_REGION_W2T || r == MOE_REGION_W13S || r == MOE_REGION_W2S;
+}
+
+// A region of the call in progress: the create-time weight tiles are always
+// the workspace's; the others come from the current per-call layout.
 template <typename T>
 T* region(moe_layer* l, int r) {
-  return reinterpret_cast<T*>(l->ws + l->L.off[r]);
+  if (is_weight_region(r)) return reinterpret_cast<T*>(l->ws + l->L.off[r]);
+  return reinterpret_cast<T*>(l->cur_base + l->cur_L->off[r]);
 }
 
 hipEvent_t take_event(moe_layer* l) {
@@ -79,15 +92,15 @@ moe::CompactArgs compact_args(moe_layer* l, int32_t T) {
   ca.staged_idx = region<int32_t>(l, MOE_REGION_STAGED_IDX);
   ca.routes = routes;
   ca.num_experts = l->cfg.num_experts;
-  ca.row_cap = (int32_t)l->L.row_cap;
+  ca.row_cap = (int32_t)l->cur_L->row_cap;
   ca.block_m = l->tac.block_m;
   ca.blocks = moe::compact_blocks_for(T, l->cfg.top_k);
   ca.chunk = moe::compact_chunk_routes(T, l->cfg.top_k);
   ca.hdr = region<uint32_t>(l, MOE_REGION_STATUS);
   // internal region: bases [compact_blocks, E], status [compact_blocks], arrival counter
   ca.blk_base = region<int32_t>(l, moe::kRegionBlkBase);
-  ca.blk_status = reinterpret_cast<uint32_t*>(ca.blk_base + l->L.compact_blocks * l->cfg.num_experts);
-  ca.arrive = ca.blk_base + l->L.compact_blocks * (l->cfg.num_experts + 1);
+  ca.blk_status = reinterpret_cast<uint32_t*>(ca.blk_base + l->cur_L->compact_blocks * l->cfg.num_experts);
+  ca.arrive = ca.blk_base + l->cur_L->compact_blocks * (l->cfg.num_experts + 1);
   ca.counts = region<int32_t>(l, MOE_REGION_COUNTS);
   ca.offsets = region<int32_t>(l, MOE_REGION_OFFSETS);
   ca.sorted_route = region<int32_t>(l, MOE_REGION_SORTED_ROUTE);
@@ -217,16 +230,19 @@ extern "C" moe_status_t moe_layer_create(const moe_config_t* cfg, int32_t expect
     return hip_fail("weight transform launch");
   }
   l->prof_mask = 0;
+  l->cur_base = l->ws;
+  l->cur_L = &l->L;
+  l->cur_max_rows = max_rows;
   memset(l->ms, 0, sizeof(l->ms));
   memset(l->launches, 0, sizeof(l->launches));
   *out = l;
   return MOE_OK;
 }
 
-extern "C" moe_status_t moe_stage_inputs(moe_layer_t* l, const void* x, const float* x_scale,
-                                         const int32_t* topk_idx, const float* topk_w, int32_t num_tokens,
-                                         void* out_bf16, void* stream) {
-  moe::clear_error();
+namespace {
+
+moe_status_t stage_impl(moe_layer_t* l, const void* x, const float* x_scale, const int32_t* topk_idx,
+                        const float* topk_w, int32_t num_tokens, void* out_bf16, void* stream) {
   if (!l) return moe::fail(MOE_ERR_INVALID_ARG, "layer is NULL");
   if (num_tokens < 0) return moe::fail(MOE_ERR_INVALID_ARG, "num_tokens %d < 0", num_tokens);
   if (num_tokens > l->max_rows)
@@ -248,7 +264,7 @@ extern "C" moe_status_t moe_stage_inputs(moe_layer_t* l, const void* x, const fl
   a.topk_idx = topk_idx;
   a.topk_w = topk_w;
   a.tokens = num_tokens;
-  a.max_rows = l->max_rows;
+  a.max_rows = l->cur_max_rows;
   a.hidden = l->cfg.hidden;
   a.top_k = l->cfg.top_k;
   a.num_experts = l->cfg.num_experts;
@@ -259,7 +275,7 @@ extern "C" moe_status_t moe_stage_inputs(moe_layer_t* l, const void* x, const fl
   a.staged_w = region<float>(l, MOE_REGION_STAGED_W);
   a.xq = region<uint8_t>(l, MOE_REGION_XQ);
   a.xs = region<float>(l, MOE_REGION_XS);
-  a.x_plane = (int64_t)l->L.rows_x * l->cfg.hidden;
+  a.x_plane = (int64_t)l->cur_L->rows_x * l->cfg.hidden;
   a.xs_mx = region<uint32_t>(l, MOE_REGION_XS);
   // One launch stages and compacts; a compaction over several workgroups
   // leaves its scatter to the forward.
@@ -273,8 +289,7 @@ extern "C" moe_status_t moe_stage_inputs(moe_layer_t* l, const void* x, const fl
   return MOE_OK;
 }
 
-extern "C" moe_status_t moe_layer_forward(moe_layer_t* l, void* stream) {
-  moe::clear_error();
+moe_status_t forward_impl(moe_layer_t* l, void* stream) {
   if (!l) return moe::fail(MOE_ERR_INVALID_ARG, "layer is NULL");
   if (l->staged_tokens < 0) return moe::fail(MOE_ERR_STATE, "moe_stage_inputs has not been called");
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -293,7 +308,7 @@ extern "C" moe_status_t moe_layer_forward(moe_layer_t* l, void* stream) {
     moe::MxGemmArgs m1;
     memset(&m1, 0, sizeof(m1));
     m1.a = region<uint8_t>(l, MOE_REGION_XQ);
-    m1.a_plane = (int64_t)l->L.rows_x * c.hidden;
+    m1.a_plane = (int64_t)l->cur_L->rows_x * c.hidden;
     m1.a_scale = region<uint32_t>(l, MOE_REGION_XS);
     m1.a_mode = 1;
     m1.sorted_route = ca.sorted_route;
@@ -308,7 +323,7 @@ extern "C" moe_status_t moe_layer_forward(moe_layer_t* l, void* stream) {
     m1.offsets = ca.offsets;
     m1.hdr = ca.hdr;
     m1.hq = region<uint8_t>(l, MOE_REGION_HQ);
-    m1.h_plane = l->L.row_cap * c.intermediate;
+    m1.h_plane = l->cur_L->row_cap * c.intermediate;
     m1.hs = region<uint32_t>(l, MOE_REGION_HS);
     m1.grid = l->grid_fc1;
     m1.w_e5m2 = c.weight_format == MOE_WEIGHT_MXFP8_E5M2;
@@ -368,7 +383,7 @@ extern "C" moe_status_t moe_layer_forward(moe_layer_t* l, void* stream) {
   if (!persistent) {
     p = prof_begin(l, MOE_KERNEL_FC1, s);
     if (moe::launch_fc1(g1, l->tac.block_m, stream) != 0) return hip_fail("fc1 launch");
-    if (unfused && moe::launch_swiglu_quant(g1.gateup, (int32_t)l->L.row_cap, c.intermediate, g1.hdr, g1.hq, g1.hs,
+    if (unfused && moe::launch_swiglu_quant(g1.gateup, (int32_t)l->cur_L->row_cap, c.intermediate, g1.hdr, g1.hq, g1.hs,
                                             stream) != 0)
       return hip_fail("swiglu launch");
     prof_end(l, p, s);
@@ -411,6 +426,79 @@ extern "C" moe_status_t moe_layer_forward(moe_layer_t* l, void* stream) {
   prof_end(l, p, s);
 
   return g2.fc.out ? MOE_OK : combine(l, T, s, stream);
+}
+
+}  // namespace
+
+extern "C" moe_status_t moe_stage_inputs(moe_layer_t* l, const void* x, const float* x_scale,
+                                         const int32_t* topk_idx, const float* topk_w, int32_t num_tokens,
+                                         void* out_bf16, void* stream) {
+  moe::clear_error();
+  return stage_impl(l, x, x_scale, topk_idx, topk_w, num_tokens, out_bf16, stream);
+}
+
+extern "C" moe_status_t moe_layer_forward(moe_layer_t* l, void* stream) {
+  moe::clear_error();
+  return forward_impl(l, stream);
+}
+
+// Stage + forward with every per-call region in the library's static device
+// scratch (moe_noalloc.hip) instead of the workspace: no device memory is
+// allocated, and the handle's own staged batch is left as it was.
+extern "C" moe_status_t moe_layer_forward_noalloc(moe_layer_t* l, const void* x, const float* x_scale,
+                                                  const int32_t* topk_idx, const float* topk_w,
+                                                  int32_t num_tokens, void* out_bf16, uint32_t* status_bits,
+                                                  void* stream) {
+  moe::clear_error();
+  if (!l) return moe::fail(MOE_ERR_INVALID_ARG, "layer is NULL");
+  if (num_tokens < 0) return moe::fail(MOE_ERR_INVALID_ARG, "num_tokens %d < 0", num_tokens);
+  if (num_tokens > l->max_rows)
+    return moe::fail(MOE_ERR_CAPACITY, "num_tokens %d exceeds max_rows %d", num_tokens, l->max_rows);
+  if ((uintptr_t)status_bits & 3) return moe::fail(MOE_ERR_INVALID_ARG, "status_bits must be 4-byte aligned");
+  uint8_t* base = nullptr;
+  size_t cap = 0;
+  if (moe::noalloc_scratch(&base, &cap) != 0) return hip_fail("device scratch address");
+  // rows as in the call; route rows held as the layer holds them (never
+  // more than the call's routes), so routes drop exactly as they would in
+  // the workspace
+  const moe::Layout S = moe::compute_scratch_layout(l->cfg, l->tac, num_tokens, l->L.row_cap);
+  if (S.total > cap)
+    return moe::fail(MOE_ERR_CAPACITY,
+                     "num_tokens %d needs %zu bytes of per-call regions; the no-allocation forward holds %zu",
+                     num_tokens, S.total, cap);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // The scratch keeps the last call's contents (of any layer on this
+  // device): what must start at zero is cleared by a fill kernel.
+  if (moe::launch_fill_zero(reinterpret_cast<uint32_t*>(base + S.off[moe::kRegionBlkBase]),
+                            (int64_t)(S.size[moe::kRegionBlkBase] / 4), stream) != 0)
+    return hip_fail("scratch clear");
+  if ((l->cfg.flags & MOE_FLAG_FUSED_COMBINE) &&
+      moe::launch_fill_zero(reinterpret_cast<uint32_t*>(base + S.off[MOE_REGION_ARRIVE]),
+                            (int64_t)(S.size[MOE_REGION_ARRIVE] / 4), stream) != 0)
+    return hip_fail("scratch clear");
+  // run on the scratch, then put the handle back as it was
+  const int32_t staged = l->staged_tokens;
+  const bool compacted = l->compacted;
+  void* out = l->out;
+  const uint32_t prof = l->prof_mask;
+  l->cur_base = base;
+  l->cur_L = &S;
+  l->cur_max_rows = num_tokens > 0 ? num_tokens : 1;
+  l->prof_mask = 0;  // event records would create events
+  moe_status_t st = stage_impl(l, x, x_scale, topk_idx, topk_w, num_tokens, out_bf16, stream);
+  if (st == MOE_OK) st = forward_impl(l, stream);
+  if (st == MOE_OK && status_bits &&
+      hipMemcpyAsync(status_bits, base + S.off[MOE_REGION_STATUS] + 4 * moe::kHdrStatus, 4,
+                     hipMemcpyDeviceToDevice, s) != hipSuccess)
+    st = hip_fail("status copy");
+  l->cur_base = l->ws;
+  l->cur_L = &l->L;
+  l->cur_max_rows = l->max_rows;
+  l->prof_mask = prof;
+  l->staged_tokens = staged;
+  l->compacted = compacted;
+  l->out = out;
+  return st;
 }
 
 extern "C" moe_status_t moe_read_status(moe_layer_t* l, void* stream, uint32_t* bits) {

@@ -108,16 +108,16 @@ moe_status_t validate_layout(const moe_config_t& cfg, const Layout& L) {
   return MOE_OK;
 }
 
-Layout compute_layout(const moe_config_t& cfg, const Tactic& t, int32_t max_rows, float capacity_factor) {
+// Regions for max_rows tokens holding row_cap route rows; the create-time
+// weight tiles are sized only with `weights`.
+static Layout layout_for(const moe_config_t& cfg, const Tactic& t, int32_t max_rows, int64_t row_cap, bool weights) {
   Layout L;
   memset(&L, 0, sizeof(L));
   const int64_t K = cfg.top_k, H = cfg.hidden, I = cfg.intermediate, E = cfg.num_experts;
   const bool mx = cfg.act_format == MOE_ACT_BF16;  // MXFP8 weights x BF16 activations
   L.route_slots = (int64_t)max_rows * K;
   L.rows_x = (cfg.flags & MOE_FLAG_PER_ROUTE_STAGING) ? L.route_slots : max_rows;
-  double cap = ceil((double)capacity_factor * (double)L.route_slots);
-  L.row_cap = cap >= (double)L.route_slots ? L.route_slots : (int64_t)cap;
-  if (L.row_cap < 1) L.row_cap = 1;
+  L.row_cap = row_cap < 1 ? 1 : row_cap;
   L.max_m_tiles = (L.row_cap + t.block_m - 1) / t.block_m + E;
   L.compact_blocks = compact_blocks_for(max_rows, cfg.top_k);
 
@@ -135,11 +135,13 @@ Layout compute_layout(const moe_config_t& cfg, const Tactic& t, int32_t max_rows
   L.size[MOE_REGION_Y] = L.row_cap * H * 2;
   L.size[MOE_REGION_TILES] = L.max_m_tiles * 4 * 4;
   // create-time tiled copies of the e4m3 weights (FC2 padded to 256-row tiles)
-  L.size[MOE_REGION_W13T] = E * (2 * I) * H;
-  L.size[MOE_REGION_W2T] = E * ((H + 255) / 256 * 256) * I;
-  // MX: one 1 KB exponent tile per 32 KB code tile
-  L.size[MOE_REGION_W13S] = mx ? L.size[MOE_REGION_W13T] / 32 : 0;
-  L.size[MOE_REGION_W2S] = mx ? L.size[MOE_REGION_W2T] / 32 : 0;
+  if (weights) {
+    L.size[MOE_REGION_W13T] = E * (2 * I) * H;
+    L.size[MOE_REGION_W2T] = E * ((H + 255) / 256 * 256) * I;
+    // MX: one 1 KB exponent tile per 32 KB code tile
+    L.size[MOE_REGION_W13S] = mx ? L.size[MOE_REGION_W13T] / 32 : 0;
+    L.size[MOE_REGION_W2S] = mx ? L.size[MOE_REGION_W2T] / 32 : 0;
+  }
   L.size[MOE_REGION_GATEUP] = (cfg.flags & MOE_FLAG_UNFUSED_FC1) ? L.row_cap * 2 * I * 4 : 0;
   L.size[MOE_REGION_READY] = (cfg.flags & MOE_FLAG_PERSISTENT_FFN) ? L.max_m_tiles * 4 : 0;
   L.size[MOE_REGION_ARRIVE] = (cfg.flags & MOE_FLAG_FUSED_COMBINE) ? (int64_t)max_rows * ((H + 255) / 256) * 4 : 0;
@@ -152,6 +154,18 @@ Layout compute_layout(const moe_config_t& cfg, const Tactic& t, int32_t max_rows
   }
   L.total = off;
   return L;
+}
+
+Layout compute_layout(const moe_config_t& cfg, const Tactic& t, int32_t max_rows, float capacity_factor) {
+  const int64_t slots = (int64_t)max_rows * cfg.top_k;
+  const double cap = ceil((double)capacity_factor * (double)slots);
+  return layout_for(cfg, t, max_rows, cap >= (double)slots ? slots : (int64_t)cap, true);
+}
+
+Layout compute_scratch_layout(const moe_config_t& cfg, const Tactic& t, int32_t tokens, int64_t layer_row_cap) {
+  const int32_t rows = tokens > 0 ? tokens : 1;
+  const int64_t slots = (int64_t)rows * cfg.top_k;
+  return layout_for(cfg, t, rows, layer_row_cap < slots ? layer_row_cap : slots, false);
 }
 
 }  // namespace moe

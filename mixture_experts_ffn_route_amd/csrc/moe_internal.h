@@ -65,6 +65,13 @@ moe_status_t validate_config(const moe_config_t* cfg, int32_t expected_m, int32_
                              float capacity_factor);
 Tactic choose_tactic(const moe_config_t& cfg, int32_t expected_m);
 Layout compute_layout(const moe_config_t& cfg, const Tactic& t, int32_t max_rows, float capacity_factor);
+// The per-call regions of one call of `tokens` tokens (no weight tiles),
+// holding min(layer_row_cap, tokens * K) route rows: routes drop exactly as
+// in the layer's workspace.
+Layout compute_scratch_layout(const moe_config_t& cfg, const Tactic& t, int32_t tokens, int64_t layer_row_cap);
+// Device address and size of the library's static scratch on the current
+// device (moe_noalloc.hip); 0 on success.
+int noalloc_scratch(uint8_t** base, size_t* bytes);
 moe_status_t fail(moe_status_t s, const char* fmt, ...);
 
 // ---------------------------------------------------------------------------

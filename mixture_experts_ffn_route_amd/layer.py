@@ -63,6 +63,17 @@ class MoELayer:
     def forward(self) -> None:
         L.moe_layer_forward(self.handle, self._stream())
 
+    def forward_noalloc(self, x: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor, out: torch.Tensor,
+                        x_scale: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None) -> None:
+        """Stage + forward with the per-call regions in the library's static
+        device scratch (moe_layer_forward_noalloc): ``out`` and the optional
+        int32 ``status`` word are caller tensors, nothing is allocated."""
+        for t in (x, topk_idx, topk_w, out) + tuple(t for t in (x_scale, status) if t is not None):
+            if not t.is_contiguous():
+                raise ValueError("inputs must be contiguous")
+        L.moe_layer_forward_noalloc(self.handle, _ptr(x), _ptr(x_scale), _ptr(topk_idx), _ptr(topk_w), x.shape[0],
+                                    _ptr(out), _ptr(status), self._stream())
+
     def status(self) -> int:
         return L.moe_read_status(self.handle, self._stream())
 

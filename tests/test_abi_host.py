@@ -149,6 +149,9 @@ def test_null_handle_calls_fail_cleanly():
         assert ei.value.status == L.MOE_ERR_INVALID_ARG
     with pytest.raises(L.MoEError):
         L.moe_stage_inputs(0, 0, 0, 0, 0, 1, 0, 0)
+    with pytest.raises(L.MoEError) as ei:
+        L.moe_layer_forward_noalloc(0, 0, 0, 0, 0, 1, 0)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARG
     L.moe_layer_destroy(0)  # no-op
 
 
