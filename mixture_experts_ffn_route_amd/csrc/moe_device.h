@@ -120,26 +120,20 @@ struct Promo {
 };
 
 // One K-block: returns the accumulator ratio r and sets `sh` to the E8M0
-// byte (127 + e - ref, at least 0) of the block's MFMA.
+// byte (127 + e - ref, at least 0) of the block's MFMA.  Branch-free (the
+// three cases are selected), so that the promotion threads of a wave, which
+// take different cases, stay on one path.
 __device__ __forceinline__ float promo_step(float sx, float sw, Promo& p, int& sh) {
   const float m = __builtin_amdgcn_frexp_mantf(sx) * __builtin_amdgcn_frexp_mantf(sw);
   const int e = __builtin_amdgcn_frexp_expf(sx) + __builtin_amdgcn_frexp_expf(sw);
-  float r;
-  if (m == 0.f) {
-    r = 1.f;
-    sh = 0;
-  } else if (p.m == 0.f) {
-    r = 0.f;
-    p.m = m;
-    p.e = e;
-    sh = 127;
-  } else {
-    const int ref = max(p.e, e);
-    r = __builtin_amdgcn_ldexpf(p.m * __builtin_amdgcn_rcpf(m), p.e - ref);
-    p.m = m;
-    p.e = ref;
-    sh = max(127 + e - ref, 0);
-  }
+  const bool zero = m == 0.f;      // the block adds nothing
+  const bool first = p.m == 0.f;   // the first block with a nonzero scale starts the sum
+  const int ref = max(p.e, e);
+  const float ratio = __builtin_amdgcn_ldexpf(p.m * __builtin_amdgcn_rcpf(m), p.e - ref);
+  const float r = zero ? 1.f : (first ? 0.f : ratio);
+  sh = zero ? 0 : (first ? 127 : max(127 + e - ref, 0));
+  p.e = zero ? p.e : (first ? e : ref);
+  p.m = zero ? p.m : m;
   return r;
 }
 

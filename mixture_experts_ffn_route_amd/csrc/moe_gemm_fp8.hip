@@ -119,7 +119,18 @@ __device__ __forceinline__ v8i lds_frag2(const lds_u8* lo_p, const lds_u8* hi_p)
 // fills across the loop back-edge, never drains the ring; the K loop waits
 // on the vector-memory counter itself.  The "memory" clobber keeps every LDS
 // access in program order around these instructions.
-__device__ __forceinline__ uint32_t lds_addr(const lds_u8* p) { return (uint32_t)(uintptr_t)p; }
+// LDS and global bases of the DMAs are wave-uniform; readfirstlane says so
+// (the asm takes them in SGPRs), and costs nothing where the compiler
+// already holds them in SGPRs.
+__device__ __forceinline__ uint32_t lds_addr(const lds_u8* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ void dma4(const float* src, const lds_u8* lds_wave_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                :: "v"(src), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
@@ -131,7 +142,7 @@ __device__ __forceinline__ void dma4(const float* src, const lds_u8* lds_wave_ba
 // loads it would move the LDS destination as well as the source.
 __device__ __forceinline__ void dma16o(const void* base, uint32_t off, const lds_u8* lds_wave_base) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(off), "s"(base), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
+               :: "v"(off), "s"(uniform_ptr(base)), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
 }
 // The weight stream of a tile that no other workgroup reads: non-temporal,
 // so the lines do not displace reused data on their way through the
@@ -139,11 +150,11 @@ __device__ __forceinline__ void dma16o(const void* base, uint32_t off, const lds
 // default policy).
 __device__ __forceinline__ void dma16o_nt(const void* base, uint32_t off, const lds_u8* lds_wave_base) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
-               :: "v"(off), "s"(base), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
+               :: "v"(off), "s"(uniform_ptr(base)), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4o(const void* base, uint32_t off, const lds_u8* lds_wave_base) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
-               :: "v"(off), "s"(base), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
+               :: "v"(off), "s"(uniform_ptr(base)), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
 }
 
 // Scale loads of the persistent FC2 phase read rows that FC1 tiles on other
@@ -153,7 +164,7 @@ template <bool kCoherent>
 __device__ __forceinline__ void dma4o_scale(const void* base, uint32_t off, const lds_u8* lds_wave_base) {
   if constexpr (kCoherent)
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1 sc1"
-                 :: "v"(off), "s"(base), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
+                 :: "v"(off), "s"(uniform_ptr(base)), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
   else
     dma4o(base, off, lds_wave_base);
 }
@@ -300,7 +311,6 @@ int launch_fc1_fc2(const GemmArgs& a1, const GemmArgs& a2, const PersistArgs& q,
     case 32: return launch_persist<32>(a1, a2, q, grid, stream);
     case 64: return launch_persist<64>(a1, a2, q, grid, stream);
     case 128: return launch_persist<128>(a1, a2, q, grid, stream);
-    case 256: return launch_persist<256>(a1, a2, q, grid, stream);
   }
   return -1;
 }
@@ -318,15 +328,23 @@ int gemm_persist_max_workgroups_per_cu(int block_m) {
     case 16: return occ_persist<16>();
     case 32: return occ_persist<32>();
     case 64: return occ_persist<64>();
-    case 128: return occ_persist<128>();
-    default: return occ_persist<256>();
+    default: return occ_persist<128>();
   }
 }
 
+#include "moe_gemm_fp8_pp.inc"
+
 template <int BT, bool FC1>
 static int launch_one(const GemmArgs& a, void* stream) {
-  hipLaunchKernelGGL((gemm_fp8_kernel<BT, FC1>), dim3(a.grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
-                     a);
+  if constexpr (BT == 256) {
+    // 256-token tiles: the ping-pong schedule (the tactic gives the variants
+    // with a gate/up output or the fused combine 128-token tiles)
+    if (a.gateup != nullptr || a.fc.out != nullptr) return -1;
+    hipLaunchKernelGGL((gemm_fp8_pp_kernel<FC1>), dim3(a.grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream), a);
+  } else {
+    hipLaunchKernelGGL((gemm_fp8_kernel<BT, FC1>), dim3(a.grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                       a);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -348,7 +366,12 @@ int launch_fc2(const GemmArgs& a, int block_m, void* stream) { return launch_bt<
 template <int BT, bool FC1>
 static int occ() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_fp8_kernel<BT, FC1>, kThreads, 0) != hipSuccess) return 1;
+  hipError_t r;
+  if constexpr (BT == 256)
+    r = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_fp8_pp_kernel<FC1>, kThreads, 0);
+  else
+    r = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_fp8_kernel<BT, FC1>, kThreads, 0);
+  if (r != hipSuccess) return 1;
   return n > 0 ? n : 1;
 }
 

@@ -87,7 +87,12 @@ Tactic choose_tactic(const moe_config_t& cfg, int32_t expected_m) {
   Tactic t;
   t.bucket = token_bucket(expected_m);
   t.block_n = 256;
-  const int cap = is_mx(cfg.weight_format) ? 128 : 256;
+  // 256-token tiles run the ping-pong FP8 kernel, which has no gate/up
+  // output, fused combine or persistent form: those variants (and the MX
+  // path, whose stage holds two activation terms) stop at 128.
+  const bool cap128 = is_mx(cfg.weight_format) ||
+                      (cfg.flags & (MOE_FLAG_UNFUSED_FC1 | MOE_FLAG_FUSED_COMBINE | MOE_FLAG_PERSISTENT_FFN));
+  const int cap = cap128 ? 128 : 256;
   t.block_m = t.bucket <= 16 ? 16 : (t.bucket >= cap ? cap : t.bucket);
   t.stages = t.block_m >= 256 ? 2 : (t.block_m >= 64 ? 3 : 4);
   if (is_mx(cfg.weight_format)) t.stages = t.block_m >= 128 ? 2 : (t.block_m >= 32 ? 3 : 4);

@@ -57,7 +57,7 @@ CASES = [
     # (shape, expected_m, weights, masked fraction)
     ("tiny", None, False, 0.0),
     ("small", None, False, 0.25),   # fully and partly masked tokens
-    ("small", 4096, False, 0.0),    # 256-token tiles
+    ("small", 4096, False, 0.0),    # 128-token fused tiles against the 256-token ping-pong FC2
     ("small", 8, False, 0.25),      # 16-token tiles
     ("odd", None, False, 0.25),     # H = 384: the last 256-column slice is half full
     ("small", None, "e4m3", 0.25),  # MXFP8 x BF16 FC2

@@ -72,7 +72,7 @@ CASES = [
     ("small", 8, 0.0, ()),          # 16-row tiles
     ("small", 24, 0.25, ()),        # 32-row tiles
     ("small", 48, 0.0, ()),         # 64-row tiles
-    ("small", 4096, 0.0, ()),       # 256-row tiles
+    ("small", 4096, 0.0, ()),       # 128-row persistent tiles against the 256-row ping-pong launches
     ("odd", None, 0.25, ()),        # H = 384
     ("small", None, 0.25, ("fused",)),  # with the fused last-arriver combine
 ]
@@ -86,7 +86,10 @@ def test_persistent_equals_two_launches(name, expected_m, masked, extra):
     more = [L.MOE_FLAG_FUSED_COMBINE] if "fused" in extra else []
     sep = make_layer(shape, dev, expected_m=expected_m)
     per = make_layer(shape, dev, expected_m=expected_m, flags=_flags(*more))
-    assert sep.tactic()["block_m"] == per.tactic()["block_m"]
+    # the persistent form stops at 128-row tiles; the two launches it is
+    # compared with may use 256 (the ping-pong kernel): every tile computes
+    # the same bits
+    assert per.tactic()["block_m"] == min(sep.tactic()["block_m"], 128)
     _compare(shape, sep, per, dev)
 
 
