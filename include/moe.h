@@ -121,7 +121,15 @@ enum {
    * flashinfer PR #4688: persistent kernel with fc1_done readiness flags).
    * Same arithmetic, same bits.  The h rows are then stored write-through so
    * that a tile on another XCD can read them. */
-  MOE_FLAG_PERSISTENT_FFN = 16u
+  MOE_FLAG_PERSISTENT_FFN = 16u,
+  /* With MOE_FLAG_UNFUSED_FC1 only: the FC1 GEMM rounds its gate/up output
+   * to bfloat16 (round to nearest even) and stores that in
+   * MOE_REGION_GATEUP; SwiGLU and the requantisation then read the BF16
+   * values.  This is the unfused path's own BF16 gate/up buffer (PR #4069,
+   * Description: the unfused FC1 stores a BF16 gate/up buffer before the
+   * SwiGLU, and stays the maintained reference), so h differs from the fused
+   * epilogue's by that rounding.  Costs a 2I x 2-byte row per route. */
+  MOE_FLAG_BF16_GATEUP = 32u
 };
 
 /* Device status bits (moe_read_status). */
@@ -189,7 +197,8 @@ enum {
   MOE_REGION_W2T = 14,          /* e4m3 w2 tiled at create: [E, ceil(H/256), I/128] tiles of 32 KB */
   MOE_REGION_W13S = 15,         /* MXFP8: w13 E8M0 tiled at create, 1 KB per w13 tile (empty for FP8) */
   MOE_REGION_W2S = 16,          /* MXFP8: w2 E8M0 tiled at create, 1 KB per w2 tile (empty for FP8) */
-  MOE_REGION_GATEUP = 17,       /* MOE_FLAG_UNFUSED_FC1: float32 [row_cap, 2I] gate then up columns (else empty) */
+  MOE_REGION_GATEUP = 17,       /* MOE_FLAG_UNFUSED_FC1: float32 [row_cap, 2I] gate then up columns (bfloat16 bits
+                                 * with MOE_FLAG_BF16_GATEUP; else empty) */
   MOE_REGION_ARRIVE = 18,       /* MOE_FLAG_FUSED_COMBINE: int32 [max_rows, ceil(H/256)] arrival counters,
                                    zero between forwards (else empty) */
   MOE_REGION_READY = 19         /* MOE_FLAG_PERSISTENT_FFN: int32 [max_m_tiles] finished FC1 column tiles

@@ -35,6 +35,7 @@ MOE_FLAG_PER_ROUTE_STAGING = 2
 MOE_FLAG_UNFUSED_FC1 = 4
 MOE_FLAG_FUSED_COMBINE = 8
 MOE_FLAG_PERSISTENT_FFN = 16
+MOE_FLAG_BF16_GATEUP = 32
 MOE_DEV_BAD_EXPERT = 1
 MOE_DEV_DUPLICATE = 2
 MOE_DEV_NONFINITE = 4

@@ -379,12 +379,13 @@ moe_status_t forward_impl(moe_layer_t* l, void* stream) {
   g1.grid = l->grid_fc1;
   const bool unfused = (c.flags & MOE_FLAG_UNFUSED_FC1) != 0;
   g1.gateup = unfused ? region<float>(l, MOE_REGION_GATEUP) : nullptr;
+  g1.gateup_bf16 = (c.flags & MOE_FLAG_BF16_GATEUP) != 0;
   const bool persistent = (c.flags & MOE_FLAG_PERSISTENT_FFN) != 0;
   if (!persistent) {
     p = prof_begin(l, MOE_KERNEL_FC1, s);
     if (moe::launch_fc1(g1, l->tac.block_m, stream) != 0) return hip_fail("fc1 launch");
-    if (unfused && moe::launch_swiglu_quant(g1.gateup, (int32_t)l->cur_L->row_cap, c.intermediate, g1.hdr, g1.hq, g1.hs,
-                                            stream) != 0)
+    if (unfused && moe::launch_swiglu_quant(g1.gateup, g1.gateup_bf16 != 0, (int32_t)l->cur_L->row_cap,
+                                            c.intermediate, g1.hdr, g1.hq, g1.hs, stream) != 0)
       return hip_fail("swiglu launch");
     prof_end(l, p, s);
   }

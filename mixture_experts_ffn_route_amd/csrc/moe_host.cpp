@@ -52,8 +52,10 @@ moe_status_t validate_config(const moe_config_t* cfg, int32_t expected_m, int32_
   if (cfg->top_k > cfg->num_experts)
     return fail(MOE_ERR_INVALID_ARG, "top_k %d exceeds num_experts %d", cfg->top_k, cfg->num_experts);
   if (cfg->flags & ~(uint32_t)(MOE_FLAG_CHECK_ROUTES | MOE_FLAG_PER_ROUTE_STAGING | MOE_FLAG_UNFUSED_FC1 |
-                               MOE_FLAG_FUSED_COMBINE | MOE_FLAG_PERSISTENT_FFN))
+                               MOE_FLAG_FUSED_COMBINE | MOE_FLAG_PERSISTENT_FFN | MOE_FLAG_BF16_GATEUP))
     return fail(MOE_ERR_INVALID_ARG, "unknown flag bits 0x%x", cfg->flags);
+  if ((cfg->flags & MOE_FLAG_BF16_GATEUP) && !(cfg->flags & MOE_FLAG_UNFUSED_FC1))
+    return fail(MOE_ERR_INVALID_ARG, "MOE_FLAG_BF16_GATEUP selects the unfused FC1's gate/up type; it needs MOE_FLAG_UNFUSED_FC1");
   if (cfg->weight_format == MOE_WEIGHT_E4M3_BLOCK128) {
     if (cfg->act_format != MOE_ACT_E4M3_1X128)
       return fail(MOE_ERR_UNSUPPORTED, "E4M3_BLOCK128 weights need E4M3_1X128 activations");
@@ -147,7 +149,8 @@ static Layout layout_for(const moe_config_t& cfg, const Tactic& t, int32_t max_r
     L.size[MOE_REGION_W13S] = mx ? L.size[MOE_REGION_W13T] / 32 : 0;
     L.size[MOE_REGION_W2S] = mx ? L.size[MOE_REGION_W2T] / 32 : 0;
   }
-  L.size[MOE_REGION_GATEUP] = (cfg.flags & MOE_FLAG_UNFUSED_FC1) ? L.row_cap * 2 * I * 4 : 0;
+  L.size[MOE_REGION_GATEUP] =
+      (cfg.flags & MOE_FLAG_UNFUSED_FC1) ? L.row_cap * 2 * I * ((cfg.flags & MOE_FLAG_BF16_GATEUP) ? 2 : 4) : 0;
   L.size[MOE_REGION_READY] = (cfg.flags & MOE_FLAG_PERSISTENT_FFN) ? L.max_m_tiles * 4 : 0;
   L.size[MOE_REGION_ARRIVE] = (cfg.flags & MOE_FLAG_FUSED_COMBINE) ? (int64_t)max_rows * ((H + 255) / 256) * 4 : 0;
   // compaction: per-(workgroup, expert) bases, per-workgroup status bits, the arrival counter

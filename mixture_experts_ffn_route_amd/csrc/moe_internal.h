@@ -152,7 +152,8 @@ struct GemmArgs {
   // outputs
   uint8_t* hq;  float* hs; // FC1: e4m3 [R, I], scales [R, I/128]
   uint16_t* y;             // FC2: bf16 [R, H]
-  float* gateup;           // FC1, unfused: FP32 gate/up rows [R, 2I] instead of the fused epilogue
+  float* gateup;           // FC1, unfused: gate/up rows [R, 2I] instead of the fused epilogue
+  int32_t gateup_bf16;     //   ... stored as bfloat16 bits (RNE) instead of FP32
   int32_t grid;
   FusedCombineArgs fc;     // FC2: last-arriver combine into the output (fc.out null: none)
 };
@@ -170,8 +171,8 @@ struct PersistArgs {
 int launch_fc1_fc2(const GemmArgs& a1, const GemmArgs& a2, const PersistArgs& q, int block_m, int grid, void* stream);
 int gemm_persist_max_workgroups_per_cu(int block_m);
 // Unfused FC1 second half: SwiGLU + 1x128 requant of the FP32 gate/up rows.
-int launch_swiglu_quant(const float* gateup, int32_t row_cap, int32_t inter, const uint32_t* hdr, uint8_t* hq,
-                        float* hs, void* stream);
+int launch_swiglu_quant(const void* gateup, bool bf16, int32_t row_cap, int32_t inter, const uint32_t* hdr,
+                        uint8_t* hq, float* hs, void* stream);
 int launch_fc2(const GemmArgs& a, int block_m, void* stream);
 int gemm_max_workgroups_per_cu(int which, int block_m);
 

@@ -41,3 +41,24 @@ def assert_output_close(got_bits, want_bits, label=""):
     # rows the oracle leaves at +0 (every route masked) must be exactly +0
     assert np.all(np.asarray(got_bits)[zero_rows] == 0), f"{label}: masked token rows are not +0"
     return rel, frac
+
+
+# The FP8 GEMM's FP32 output (gate/up before SwiGLU) against the float64
+# product of its dequantised operands.  Per output, K-block kb adds the
+# MFMA's sum of 128 e4m3 products times the block's scale product F_kb; the
+# MFMA's error is at most 2^-10 of its largest product (measured:
+# test_gpu_mfma_accumulation), bounded here by the block maxima of |x| and
+# |w|; the promotion multiply, the MFMA's addition of the running
+# accumulator and the final multiply each round once more to FP32, at most
+# (kbs + 2) * 2^-24 * sum_k |x_k w_k| in all.
+MFMA_BETA = 2.0 ** -10
+
+
+def gemm_error_bound(x_rows, w_rows):
+    """Elementwise bound on |FP32 GEMM - exact| for x_rows [n, K] @ w_rows[m, K]^T
+    (dequantised float64 operands, K a multiple of 128)."""
+    n, K = x_rows.shape
+    kbs = K // 128
+    ax = np.abs(x_rows).reshape(n, kbs, 128).max(axis=2)
+    aw = np.abs(w_rows).reshape(w_rows.shape[0], kbs, 128).max(axis=2)
+    return MFMA_BETA * (ax @ aw.T) + (kbs + 2) * 2.0 ** -24 * (np.abs(x_rows) @ np.abs(w_rows).T)

@@ -188,6 +188,18 @@ def test_unfused_fc1_flag():
     assert ei.value.status == L.MOE_ERR_UNSUPPORTED
 
 
+def test_bf16_gateup_flag():
+    """MOE_FLAG_BF16_GATEUP halves the unfused gate/up region (BF16) and is
+    refused without MOE_FLAG_UNFUSED_FC1."""
+    unf = L.moe_workspace_query(_cfg(flags=L.MOE_FLAG_CHECK_ROUTES | L.MOE_FLAG_UNFUSED_FC1), 128, 4096, 1.0)
+    b16 = L.moe_workspace_query(_cfg(flags=L.MOE_FLAG_CHECK_ROUTES | L.MOE_FLAG_UNFUSED_FC1 | L.MOE_FLAG_BF16_GATEUP),
+                                128, 4096, 1.0)
+    assert abs((unf - b16) - 4096 * 8 * 2 * 2048 * 2) <= 256
+    with pytest.raises(L.MoEError) as ei:
+        L.moe_workspace_query(_cfg(flags=L.MOE_FLAG_CHECK_ROUTES | L.MOE_FLAG_BF16_GATEUP), 128, 4096, 1.0)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARG
+
+
 def test_fused_combine_flag():
     """MOE_FLAG_FUSED_COMBINE adds the int32 [max_rows, ceil(H/256)] arrival
     counters and is accepted with either weight format."""
