@@ -153,6 +153,60 @@ def run_cpu_baseline(inp, sample_tokens, tokens):
                       f"decode), {dt:.1f} s"}
 
 
+def slot_timer_report(args, base, flags, mx):
+    """Cycles per K-block of each phase of the 256-token GEMM kernel's two
+    slots, per GEMM and wave group (moe_debug_slot_timers), and the share of
+    the tile epilogue, over `steps` forwards of the headline workload after
+    the usual settle and warm-up.  The timed build reads a cycle counter at
+    every phase boundary, so its step time is a little longer than the plain
+    build's."""
+    import torch
+
+    from mixture_experts_ffn_route_amd import _lib as L
+    from mixture_experts_ffn_route_amd.harness import make_layer, to_device
+    from synthetic import MoEShape, make_layer_inputs
+
+    tokens = args.tokens or base.tokens
+    shape = MoEShape(tokens, base.hidden, base.intermediate, base.experts, base.top_k, base.routing)
+    dev = to_device(make_layer_inputs(shape, seed=args.seed, weight_format=args.weights))
+    layer = make_layer(shape, dev, mx=mx, flags=flags, expected_m=args.expected_m)
+    out = torch.empty((tokens, shape.hidden), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        layer.stage(dev.x, dev.topk_idx, dev.topk_w, out=out)
+        layer.forward()
+
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < args.settle_s:
+        step()
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    L.moe_debug_slot_timers()  # clears the counters
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    w = L.moe_debug_slot_timers()
+    names = ["load_dma_issue", "load_lds_and_records", "load_barrier", "mfma_slot_issue", "own_load_wait",
+             "mfma_barrier", "epilogue"]
+    rep = {"workload": f"{args.config} T={tokens}", "tactic": layer.tactic()["block_m"], "steps": args.steps,
+           "ms_per_step": round(ms, 4), "unit": "cycles per K-block per wave (epilogue: share of the kernel)"}
+    for g, gemm in ((0, "fc1"), (16, "fc2")):
+        for grp in range(2):
+            d = w[g + grp * 8: g + grp * 8 + 8]
+            kblocks = d[7]
+            if kblocks == 0:
+                continue
+            row = {n: round(d[i] / kblocks, 1) for i, n in enumerate(names[:6])}
+            row["k_block_total"] = round(sum(d[:6]) / kblocks, 1)
+            row["epilogue_share"] = round(d[6] / max(sum(d[:7]), 1), 4)
+            rep[f"{gemm}_group{grp}"] = row
+    print(json.dumps(rep), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,7 +236,13 @@ def main():
                     help="expected rows per expert, which picks the token tile (default: T*K/E)")
     ap.add_argument("--sweep", default="", help="comma-separated token counts; extra lines to --sweep-out")
     ap.add_argument("--sweep-out", default="bench_sweep.jsonl", help="file the sweep lines are appended to")
+    ap.add_argument("--slot-timers", action="store_true",
+                    help="diagnostic: load the library built with slot timers (build.py --slot-timers), run the "
+                         "headline workload and print the 256-token GEMMs' cycles per K-block and phase instead "
+                         "of the bench line")
     args = ap.parse_args()
+    if args.slot_timers:
+        os.environ["MOE_SLOT_TIMERS"] = "1"
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the layer; the library runs on one GPU, and the "
@@ -209,6 +269,10 @@ def main():
         flags |= L.MOE_FLAG_PERSISTENT_FFN
 
     cache = {}
+
+    if args.slot_timers:
+        slot_timer_report(args, base, flags, mx)
+        return
 
     def inputs_for(shape):
         """Seeded inputs of one token count; the expert weights (which do not

@@ -322,6 +322,20 @@ moe_status_t moe_layer_tactic(const moe_layer_t* layer, moe_tactic_t* tactic);
 moe_status_t moe_profile_enable(moe_layer_t* layer, uint32_t kernel_mask);
 moe_status_t moe_profile_read(moe_layer_t* layer, double* ms_total, int64_t* launches);
 
+/* Cycle counters of the 256-token FP8 GEMM kernel's slots, for measuring
+ * where its K loop spends time; not for production use.  Only a library
+ * built with slot timers (build.py --slot-timers, which compiles the
+ * counter reads into the kernel) records them; any other build returns
+ * MOE_ERR_UNSUPPORTED and writes nothing.  out: host array of `count`
+ * (>= MOE_SLOT_TIMER_WORDS) uint64, laid out [GEMM: FC1, FC2][wave group:
+ * 0, 1][word]: words 0-6 the summed cycles of load-slot DMA issue, load-slot
+ * LDS reads and records, load-slot barrier wait, MFMA-slot issue, wait for
+ * the wave's own loads, MFMA-slot barrier wait, tile epilogue; word 7 the
+ * number of K-blocks; summed over waves and launches since the previous
+ * call, which then clears them.  Synchronises the device. */
+#define MOE_SLOT_TIMER_WORDS 32
+moe_status_t moe_debug_slot_timers(uint64_t* out, int32_t count);
+
 /* Release the handle (host memory only; the workspace stays the caller's).
  * Destroying NULL is a no-op. */
 moe_status_t moe_layer_destroy(moe_layer_t* layer);

@@ -14,7 +14,11 @@ import os
 from ctypes import POINTER, Structure, c_char_p, c_double, c_float, c_int32, c_int64, c_size_t, c_uint32, c_void_p
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+# MOE_SLOT_TIMERS=1 loads the build with the 256-token GEMM's slot timers
+# (build.py --slot-timers; for moe_debug_slot_timers), never built on demand.
+SLOT_TIMERS = os.environ.get("MOE_SLOT_TIMERS", "0") == "1"
+LIB_PATH = os.path.join(_HERE, "libmoe_mi355x_slot_timers.so" if SLOT_TIMERS else "libmoe_mi355x.so")
+MOE_SLOT_TIMER_WORDS = 32
 
 # moe_status_t
 MOE_OK = 0
@@ -55,7 +59,7 @@ EXPORTS = (
     "moe_workspace_query", "moe_layer_create", "moe_stage_inputs", "moe_layer_forward",
     "moe_layer_forward_noalloc", "moe_read_status", "moe_layer_region", "moe_layer_tactic", "moe_profile_enable",
     "moe_profile_read", "moe_layer_destroy", "moe_token_bucket", "moe_status_string",
-    "moe_last_error",
+    "moe_last_error", "moe_debug_slot_timers",
 )
 
 
@@ -84,6 +88,8 @@ class moe_tactic_t(Structure):
 
 
 def _load() -> ctypes.CDLL:
+    if SLOT_TIMERS and not os.path.exists(LIB_PATH):
+        raise ImportError(f"MOE_SLOT_TIMERS=1 needs {LIB_PATH} (build.py --slot-timers)")
     if not os.path.exists(LIB_PATH):
         # nothing built yet: compile the gfx950 library (hipcc), else fail
         try:
@@ -111,6 +117,7 @@ def _load() -> ctypes.CDLL:
         "moe_profile_enable": (i32, [vp, c_uint32]),
         "moe_profile_read": (i32, [vp, POINTER(c_double), POINTER(c_int64)]),
         "moe_layer_destroy": (i32, [vp]),
+        "moe_debug_slot_timers": (i32, [vp, i32]),
         "moe_token_bucket": (i32, [i32]),
         "moe_status_string": (c_char_p, [i32]),
         "moe_last_error": (c_char_p, []),
@@ -215,3 +222,12 @@ def moe_layer_destroy(layer: int) -> None:
 
 def moe_token_bucket(tokens: int) -> int:
     return _lib.moe_token_bucket(tokens)
+
+
+def moe_debug_slot_timers():
+    """moe_debug_slot_timers: the slot cycle counters since the previous call
+    as a list of MOE_SLOT_TIMER_WORDS ints (raises MoEError with
+    MOE_ERR_UNSUPPORTED unless the timed library is loaded)."""
+    buf = (ctypes.c_uint64 * MOE_SLOT_TIMER_WORDS)()
+    _check(_lib.moe_debug_slot_timers(ctypes.cast(buf, c_void_p), MOE_SLOT_TIMER_WORDS))
+    return list(buf)

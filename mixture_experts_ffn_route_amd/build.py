@@ -20,6 +20,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+# The same library with the 256-token GEMM's slot timers compiled in
+# (moe_debug_slot_timers); loaded instead of LIB_NAME when MOE_SLOT_TIMERS=1.
+TIMERS_LIB_NAME = "libmoe_mi355x_slot_timers.so"
+TIMERS_LIB_PATH = os.path.join(PKG, TIMERS_LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = [
@@ -51,9 +55,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, verbose: bool, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -65,21 +69,25 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile and link; returns the library path.  Always rebuilds."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, slot_timers: bool = False) -> str:
+    """Compile and link; returns the library path.  Always rebuilds.
+    slot_timers: build the timed variant (TIMERS_LIB_NAME) instead."""
+    build_dir = os.path.join(BUILD, "slot_timers") if slot_timers else BUILD
+    extra = ("-DMOE_SLOT_TIMERS=1",) if slot_timers else ()
+    out = TIMERS_LIB_PATH if slot_timers else LIB_PATH
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, extra), SOURCES))
+    tmp = out + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, slot_timers="--slot-timers" in sys.argv))

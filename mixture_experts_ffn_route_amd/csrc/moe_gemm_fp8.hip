@@ -332,6 +332,13 @@ int gemm_persist_max_workgroups_per_cu(int block_m) {
   }
 }
 
+#ifndef MOE_SLOT_TIMERS
+#define MOE_SLOT_TIMERS 0
+#endif
+#if MOE_SLOT_TIMERS
+__device__ unsigned long long g_slot_timers[MOE_SLOT_TIMER_WORDS];
+#endif
+
 #include "moe_gemm_fp8_pp.inc"
 
 template <int BT, bool FC1>
@@ -387,3 +394,22 @@ int gemm_max_workgroups_per_cu(int which, int block_m) {
 }
 
 }  // namespace moe
+
+extern "C" moe_status_t moe_debug_slot_timers(uint64_t* out, int32_t count) {
+  moe::clear_error();
+#if MOE_SLOT_TIMERS
+  if (!out || count < MOE_SLOT_TIMER_WORDS)
+    return moe::fail(MOE_ERR_INVALID_ARG, "out must hold %d words", MOE_SLOT_TIMER_WORDS);
+  if (hipDeviceSynchronize() != hipSuccess ||
+      hipMemcpyFromSymbol(out, HIP_SYMBOL(moe::g_slot_timers), MOE_SLOT_TIMER_WORDS * sizeof(uint64_t)) != hipSuccess)
+    return moe::fail(MOE_ERR_HIP, "reading the slot timers failed");
+  const uint64_t zero[MOE_SLOT_TIMER_WORDS] = {};
+  if (hipMemcpyToSymbol(HIP_SYMBOL(moe::g_slot_timers), zero, sizeof(zero)) != hipSuccess)
+    return moe::fail(MOE_ERR_HIP, "clearing the slot timers failed");
+  return MOE_OK;
+#else
+  (void)out;
+  (void)count;
+  return moe::fail(MOE_ERR_UNSUPPORTED, "this library was built without slot timers (build.py --slot-timers)");
+#endif
+}

@@ -73,6 +73,7 @@ Layout compute_scratch_layout(const moe_config_t& cfg, const Tactic& t, int32_t 
 // device (moe_noalloc.hip); 0 on success.
 int noalloc_scratch(uint8_t** base, size_t* bytes);
 moe_status_t fail(moe_status_t s, const char* fmt, ...);
+void clear_error();
 
 // ---------------------------------------------------------------------------
 // Kernel launchers (moe_*.hip).  All take a hipStream_t as void*.

@@ -200,6 +200,18 @@ def test_bf16_gateup_flag():
     assert ei.value.status == L.MOE_ERR_INVALID_ARG
 
 
+def test_slot_timers_unsupported_in_the_plain_build():
+    """moe_debug_slot_timers only works in the library built with slot
+    timers; the plain build refuses it without touching the buffer."""
+    if L.SLOT_TIMERS:
+        pytest.skip("the timed library is loaded")
+    buf = (ctypes.c_uint64 * L.MOE_SLOT_TIMER_WORDS)(*([7] * L.MOE_SLOT_TIMER_WORDS))
+    st = L.lib().moe_debug_slot_timers(ctypes.cast(buf, ctypes.c_void_p), L.MOE_SLOT_TIMER_WORDS)
+    assert st == L.MOE_ERR_UNSUPPORTED
+    assert list(buf) == [7] * L.MOE_SLOT_TIMER_WORDS
+    assert "slot timers" in L.moe_last_error()
+
+
 def test_fused_combine_flag():
     """MOE_FLAG_FUSED_COMBINE adds the int32 [max_rows, ceil(H/256)] arrival
     counters and is accepted with either weight format."""
