@@ -9,7 +9,8 @@ are synthetic and already resident in HBM when timing starts.
 Headline workload: the DeepSeek-V3-like one-GPU share (H=7168, I=2048, 32
 local experts, top-8, balanced block-permutation routing, T=4096 tokens).
 The same JSON line also carries the token-sweep points where the targets
-sit (T=8 and 64: weight-streaming, HBM-bound; T=8192 and 32768: MFMA-bound),
+sit (T=8 and 64: weight-streaming, HBM-bound; T=512: between the two regimes, HBM-bound
+by FLOP per byte; T=8192 and 32768: MFMA-bound),
 each timed the same way, with its own roofline (bound chosen by the step's
 FLOP per algorithmic byte against the machine balance) and a sampled CPU
 baseline (the float64 oracle on this host).
@@ -217,7 +218,7 @@ def main():
                          "reaches its steady clock only after some 25 steps of this workload")
     ap.add_argument("--config", default="dsv3", choices=["tiny", "small", "dsv3", "skewed"])
     ap.add_argument("--tokens", type=int, default=None, help="override T of the headline workload")
-    ap.add_argument("--points", default="8,64,8192,32768",
+    ap.add_argument("--points", default="8,64,512,8192,32768",
                     help="extra token counts of the same shape timed into the JSON line ('' for none)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--weights", default="fp8_block", choices=["fp8_block", "mxfp8", "mxfp8_e5m2"],
