@@ -92,6 +92,7 @@ COUNTER_FILE = os.path.join(ROOT, "profiles", "fc1_dsv3_T4096_hbm_counters.txt")
 COUNTER_SOURCES = ["mixture_experts_ffn_route_amd/csrc/moe_gemm_fp8.hip",
                    "mixture_experts_ffn_route_amd/csrc/moe_gemm_fp8_body.inc",
                    "mixture_experts_ffn_route_amd/csrc/moe_gemm_fp8_pp.inc",
+                   "mixture_experts_ffn_route_amd/csrc/moe_gemm_fp8_stream.inc",
                    "mixture_experts_ffn_route_amd/csrc/moe_device.h",
                    "mixture_experts_ffn_route_amd/csrc/moe_store_dev.h",
                    "mixture_experts_ffn_route_amd/csrc/moe_host.cpp",
@@ -233,6 +234,10 @@ def main():
     ap.add_argument("--cpu-point-sample", type=int, default=64, help="tokens per extra point for its CPU baseline")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (reference for HBM byte counters)")
+    ap.add_argument("--no-stream", action="store_true",
+                    help="run FC2 at 64-token tiles on the LDS-ring kernel too (MOE_FLAG_NO_STREAM)")
+    ap.add_argument("--stream-fc1", action="store_true",
+                    help="run FC1 at 64-token tiles on the streaming kernel (MOE_FLAG_STREAM_FC1)")
     ap.add_argument("--expected-m", type=int, default=None,
                     help="expected rows per expert, which picks the token tile (default: T*K/E)")
     ap.add_argument("--sweep", default="", help="comma-separated token counts; extra lines to --sweep-out")
@@ -265,6 +270,10 @@ def main():
     # activation terms), so its ceiling in layer FLOPs is half the FP8 peak.
     peak = FP8_PEAK_TFLOPS / 2 if mx else FP8_PEAK_TFLOPS
     flags = L.MOE_FLAG_CHECK_ROUTES | (L.MOE_FLAG_FUSED_COMBINE if args.combine == "fused" else 0)
+    if args.no_stream:
+        flags |= L.MOE_FLAG_NO_STREAM
+    if args.stream_fc1:
+        flags |= L.MOE_FLAG_STREAM_FC1
     persistent = args.ffn == "persistent"
     if persistent:
         flags |= L.MOE_FLAG_PERSISTENT_FFN
@@ -364,7 +373,7 @@ def main():
             "flop_per_byte": round(flops / B, 1),
             "fc1_ms": round(fc1_s * 1e3, 4), "fc1_roofline": roof,
             "kernel_avg_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in prof.items()},
-            "tactic": layer.tactic()["block_m"],
+            "tactic": layer.tactic()["block_m"], "stream_depth": [layer.tactic()["stream_depth_fc1"], layer.tactic()["stream_depth_fc2"]],
         }
         log(f"[bench] T={tokens} {json.dumps(rec)}")
         if cpu_sample > 0:

@@ -129,7 +129,21 @@ enum {
    * Description: the unfused FC1 stores a BF16 gate/up buffer before the
    * SwiGLU, and stays the maintained reference), so h differs from the fused
    * epilogue's by that rounding.  Costs a 2I x 2-byte row per route. */
-  MOE_FLAG_BF16_GATEUP = 32u
+  MOE_FLAG_BF16_GATEUP = 32u,
+  /* Run FC2 at 64-token tiles on the LDS-ring GEMM kernel instead of the
+   * streaming kernel.  The streaming kernel (FP8 path without UNFUSED_FC1,
+   * FUSED_COMBINE or PERSISTENT_FFN, where the GEMM's K-blocks and column
+   * tiles come in pairs) computes two 256-row weight tiles against one
+   * 64-token tile per workgroup and loads the weights straight into a
+   * register ring two K-blocks deep.  Same arithmetic, same bits; a
+   * cross-check and comparison path. */
+  MOE_FLAG_NO_STREAM = 64u,
+  /* Run FC1 at 64-token tiles on the streaming kernel too, with
+   * non-temporal weight loads.  Faster when every expert gets about one
+   * token tile (balanced routing); slower when some experts get many tiles,
+   * whose weights several workgroups then read from HBM again.  Excludes
+   * MOE_FLAG_NO_STREAM. */
+  MOE_FLAG_STREAM_FC1 = 128u
 };
 
 /* Device status bits (moe_read_status). */
@@ -176,6 +190,9 @@ typedef struct {
   int32_t max_m_tiles;   /* bound on (expert, row-tile) pairs */
   int32_t tile_order;    /* weight tile order in MOE_REGION_W13T/W2T: 0 16x16x128 fragments,
                             1 MX-scaled operand order */
+  int32_t stream_depth_fc1;  /* K-blocks in flight per workgroup in the streaming FC1 kernel
+                                (0: the LDS-ring kernel runs) */
+  int32_t stream_depth_fc2;  /* the same for FC2 */
 } moe_tactic_t;
 
 /* Workspace regions exposed for inspection (moe_layer_region). */

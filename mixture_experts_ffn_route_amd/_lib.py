@@ -40,6 +40,8 @@ MOE_FLAG_UNFUSED_FC1 = 4
 MOE_FLAG_FUSED_COMBINE = 8
 MOE_FLAG_PERSISTENT_FFN = 16
 MOE_FLAG_BF16_GATEUP = 32
+MOE_FLAG_NO_STREAM = 64
+MOE_FLAG_STREAM_FC1 = 128
 MOE_DEV_BAD_EXPERT = 1
 MOE_DEV_DUPLICATE = 2
 MOE_DEV_NONFINITE = 4
@@ -84,6 +86,7 @@ class moe_tactic_t(Structure):
     _fields_ = [
         ("token_bucket", c_int32), ("block_m", c_int32), ("block_n", c_int32), ("grid_fc1", c_int32),
         ("grid_fc2", c_int32), ("row_cap", c_int32), ("max_m_tiles", c_int32), ("tile_order", c_int32),
+        ("stream_depth_fc1", c_int32), ("stream_depth_fc2", c_int32),
     ]
 
 

@@ -31,6 +31,7 @@ struct moe_layer {
   bool compacted;  // the staging launch also scattered the routes (one compaction workgroup)
   void* out;
   int32_t grid_fc1, grid_fc2;
+  int32_t stream_fc1, stream_fc2;  // register-ring depth of the streaming kernel per GEMM (0: LDS-ring kernel)
   int32_t grid_persist;  // MOE_FLAG_PERSISTENT_FFN: cooperative grid of the FC1->FC2 launch
   // profiling: event pairs around the launches of the classes in prof_mask
   uint32_t prof_mask;
@@ -187,9 +188,18 @@ extern "C" moe_status_t moe_layer_create(const moe_config_t* cfg, int32_t expect
   l->compacted = false;
   l->out = nullptr;
   const bool mx = moe::is_mx(cfg->weight_format);
+  // the streaming kernel serves the plain two-launch FP8 path (the variants
+  // with a gate/up output, the fused combine or one persistent launch run the
+  // LDS-ring kernel): FC2 by default, FC1 on request
+  const bool stream_ok = !mx && !(cfg->flags & (MOE_FLAG_UNFUSED_FC1 | MOE_FLAG_FUSED_COMBINE |
+                                                MOE_FLAG_PERSISTENT_FFN | MOE_FLAG_NO_STREAM));
+  l->stream_fc1 = stream_ok && (cfg->flags & MOE_FLAG_STREAM_FC1)
+                      ? moe::gemm_stream_depth(t.block_m, cfg->hidden / 128, cfg->intermediate / 128)
+                      : 0;
+  l->stream_fc2 = stream_ok ? moe::gemm_stream_depth(t.block_m, cfg->intermediate / 128, (cfg->hidden + 255) / 256) : 0;
   auto grid = [&](int which) {
     int g = cus * (mx ? moe::gemm_mx_max_workgroups_per_cu(which, t.block_m)
-                      : moe::gemm_max_workgroups_per_cu(which, t.block_m));
+                      : moe::gemm_max_workgroups_per_cu(which, t.block_m, which == 1 ? l->stream_fc1 : l->stream_fc2));
     g = (g / 8) * 8;
     return g < 8 ? 8 : g;
   };
@@ -377,6 +387,7 @@ moe_status_t forward_impl(moe_layer_t* l, void* stream) {
   g1.hq = region<uint8_t>(l, MOE_REGION_HQ);
   g1.hs = region<float>(l, MOE_REGION_HS);
   g1.grid = l->grid_fc1;
+  g1.stream_depth = l->stream_fc1;
   const bool unfused = (c.flags & MOE_FLAG_UNFUSED_FC1) != 0;
   g1.gateup = unfused ? region<float>(l, MOE_REGION_GATEUP) : nullptr;
   g1.gateup_bf16 = (c.flags & MOE_FLAG_BF16_GATEUP) != 0;
@@ -408,6 +419,7 @@ moe_status_t forward_impl(moe_layer_t* l, void* stream) {
   g2.hdr = ca.hdr;
   g2.y = region<uint16_t>(l, MOE_REGION_Y);
   g2.grid = l->grid_fc2;
+  g2.stream_depth = l->stream_fc2;
   g2.fc = fused_combine_args(l);
   if (persistent) {
     // FC1 and FC2 in one launch, timed as the FC1 class (FC2 has no launch)
@@ -534,6 +546,8 @@ extern "C" moe_status_t moe_layer_tactic(const moe_layer_t* l, moe_tactic_t* t) 
   t->row_cap = (int32_t)l->L.row_cap;
   t->max_m_tiles = (int32_t)l->L.max_m_tiles;
   t->tile_order = moe::is_mx(l->cfg.weight_format) ? moe::kTileOrderMx : moe::kTileOrder16;
+  t->stream_depth_fc1 = l->stream_fc1;
+  t->stream_depth_fc2 = l->stream_fc2;
   return MOE_OK;
 }
 

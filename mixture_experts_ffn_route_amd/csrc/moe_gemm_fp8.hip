@@ -340,9 +340,31 @@ __device__ unsigned long long g_slot_timers[MOE_SLOT_TIMER_WORDS];
 #endif
 
 #include "moe_gemm_fp8_pp.inc"
+#include "moe_gemm_fp8_stream.inc"
+
+// 64-token tiles run the streaming kernel on two column tiles per tile
+// (512 weight rows, two K-blocks = 128 KB of weights in flight) where K has
+// an even number of blocks and the column tiles pair up.
+constexpr int kStreamBT = 64, kStreamD = 2, kStreamCT = 2;
+int gemm_stream_depth(int block_m, int kbs, int n_tiles) {
+  return block_m == kStreamBT && kbs % kStreamD == 0 && n_tiles % kStreamCT == 0 ? kStreamD : 0;
+}
+
+template <bool FC1>
+static int launch_stream(const GemmArgs& a, void* stream) {
+  if (a.gateup != nullptr || a.fc.out != nullptr || a.stream_depth != kStreamD ||
+      a.k_dim % (kStreamD * kKB) != 0 || a.n_tiles % kStreamCT != 0)
+    return -1;
+  hipLaunchKernelGGL((gemm_fp8_stream_kernel<kStreamBT, kStreamD, kStreamCT, FC1>), dim3(a.grid), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
 
 template <int BT, bool FC1>
 static int launch_one(const GemmArgs& a, void* stream) {
+  if constexpr (BT == kStreamBT) {
+    if (a.stream_depth != 0) return launch_stream<FC1>(a, stream);
+  }
   if constexpr (BT == 256) {
     // 256-token tiles: the ping-pong schedule (the tactic gives the variants
     // with a gate/up output or the fused combine 128-token tiles)
@@ -371,10 +393,16 @@ int launch_fc1(const GemmArgs& a, int block_m, void* stream) { return launch_bt<
 int launch_fc2(const GemmArgs& a, int block_m, void* stream) { return launch_bt<false>(a, block_m, stream); }
 
 template <int BT, bool FC1>
-static int occ() {
+static int occ(int depth) {
   int n = 0;
   hipError_t r;
-  if constexpr (BT == 256)
+  if constexpr (BT == kStreamBT) {
+    if (depth != 0)
+      r = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_fp8_stream_kernel<kStreamBT, kStreamD, kStreamCT, FC1>,
+                                                       kThreads, 0);
+    else
+      r = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_fp8_kernel<BT, FC1>, kThreads, 0);
+  } else if constexpr (BT == 256)
     r = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_fp8_pp_kernel<FC1>, kThreads, 0);
   else
     r = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_fp8_kernel<BT, FC1>, kThreads, 0);
@@ -382,14 +410,15 @@ static int occ() {
   return n > 0 ? n : 1;
 }
 
-int gemm_max_workgroups_per_cu(int which, int block_m) {
+int gemm_max_workgroups_per_cu(int which, int block_m, int stream_depth) {
   const bool f1 = which == 1;
+  const int d = stream_depth;
   switch (block_m) {
-    case 16: return f1 ? occ<16, true>() : occ<16, false>();
-    case 32: return f1 ? occ<32, true>() : occ<32, false>();
-    case 64: return f1 ? occ<64, true>() : occ<64, false>();
-    case 128: return f1 ? occ<128, true>() : occ<128, false>();
-    default: return f1 ? occ<256, true>() : occ<256, false>();
+    case 16: return f1 ? occ<16, true>(0) : occ<16, false>(0);
+    case 32: return f1 ? occ<32, true>(d) : occ<32, false>(d);
+    case 64: return f1 ? occ<64, true>(d) : occ<64, false>(d);
+    case 128: return f1 ? occ<128, true>(d) : occ<128, false>(d);
+    default: return f1 ? occ<256, true>(0) : occ<256, false>(0);
   }
 }
 

@@ -52,8 +52,11 @@ moe_status_t validate_config(const moe_config_t* cfg, int32_t expected_m, int32_
   if (cfg->top_k > cfg->num_experts)
     return fail(MOE_ERR_INVALID_ARG, "top_k %d exceeds num_experts %d", cfg->top_k, cfg->num_experts);
   if (cfg->flags & ~(uint32_t)(MOE_FLAG_CHECK_ROUTES | MOE_FLAG_PER_ROUTE_STAGING | MOE_FLAG_UNFUSED_FC1 |
-                               MOE_FLAG_FUSED_COMBINE | MOE_FLAG_PERSISTENT_FFN | MOE_FLAG_BF16_GATEUP))
+                               MOE_FLAG_FUSED_COMBINE | MOE_FLAG_PERSISTENT_FFN | MOE_FLAG_BF16_GATEUP |
+                               MOE_FLAG_NO_STREAM | MOE_FLAG_STREAM_FC1))
     return fail(MOE_ERR_INVALID_ARG, "unknown flag bits 0x%x", cfg->flags);
+  if ((cfg->flags & MOE_FLAG_STREAM_FC1) && (cfg->flags & MOE_FLAG_NO_STREAM))
+    return fail(MOE_ERR_INVALID_ARG, "MOE_FLAG_STREAM_FC1 and MOE_FLAG_NO_STREAM exclude each other");
   if ((cfg->flags & MOE_FLAG_BF16_GATEUP) && !(cfg->flags & MOE_FLAG_UNFUSED_FC1))
     return fail(MOE_ERR_INVALID_ARG, "MOE_FLAG_BF16_GATEUP selects the unfused FC1's gate/up type; it needs MOE_FLAG_UNFUSED_FC1");
   if (cfg->weight_format == MOE_WEIGHT_E4M3_BLOCK128) {

@@ -157,6 +157,7 @@ struct GemmArgs {
   int32_t gateup_bf16;     //   ... stored as bfloat16 bits (RNE) instead of FP32
   int32_t grid;
   FusedCombineArgs fc;     // FC2: last-arriver combine into the output (fc.out null: none)
+  int32_t stream_depth;    // 64-token tiles: K-blocks in flight of the streaming kernel (0: LDS-ring kernel)
 };
 int launch_fc1(const GemmArgs& a, int block_m, void* stream);
 
@@ -175,7 +176,11 @@ int gemm_persist_max_workgroups_per_cu(int block_m);
 int launch_swiglu_quant(const void* gateup, bool bf16, int32_t row_cap, int32_t inter, const uint32_t* hdr,
                         uint8_t* hq, float* hs, void* stream);
 int launch_fc2(const GemmArgs& a, int block_m, void* stream);
-int gemm_max_workgroups_per_cu(int which, int block_m);
+// K-blocks in flight per workgroup of the streaming FP8 kernel for a GEMM
+// with `kbs` K-blocks and `n_tiles` column tiles at token tile block_m, or 0
+// where the LDS-ring kernel runs.
+int gemm_stream_depth(int block_m, int kbs, int n_tiles);
+int gemm_max_workgroups_per_cu(int which, int block_m, int stream_depth);
 
 // MXFP8-weight x BF16-activation GEMMs (moe_gemm_mx.hip).  Activations are
 // held as two e4m3 terms with their own E8M0 exponent per 32 K-elements.

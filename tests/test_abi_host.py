@@ -57,7 +57,7 @@ def _cfg(**kw):
     (dict(num_experts=0), L.MOE_ERR_UNSUPPORTED),
     (dict(num_experts=2000), L.MOE_ERR_UNSUPPORTED),
     (dict(num_experts=4, top_k=6), L.MOE_ERR_INVALID_ARG),
-    (dict(flags=0x80), L.MOE_ERR_INVALID_ARG),
+    (dict(flags=0x100), L.MOE_ERR_INVALID_ARG),
     (dict(act_format=L.MOE_ACT_BF16), L.MOE_ERR_UNSUPPORTED),
     (dict(weight_format=L.MOE_WEIGHT_MXFP8_E4M3), L.MOE_ERR_UNSUPPORTED),
     (dict(weight_format=7), L.MOE_ERR_INVALID_ARG),
@@ -186,6 +186,17 @@ def test_unfused_fc1_flag():
         L.moe_workspace_query(_cfg(weight_format=L.MOE_WEIGHT_MXFP8_E4M3, act_format=L.MOE_ACT_BF16,
                                    flags=L.MOE_FLAG_UNFUSED_FC1), 128, 4096, 1.0)
     assert ei.value.status == L.MOE_ERR_UNSUPPORTED
+
+
+def test_stream_flags():
+    """The streaming-kernel switches change no workspace size, and asking
+    for the streaming FC1 while turning streaming off is refused."""
+    base = L.moe_workspace_query(_cfg(), 128, 4096, 1.0)
+    for f in (L.MOE_FLAG_NO_STREAM, L.MOE_FLAG_STREAM_FC1):
+        assert L.moe_workspace_query(_cfg(flags=L.MOE_FLAG_CHECK_ROUTES | f), 128, 4096, 1.0) == base
+    with pytest.raises(L.MoEError) as ei:
+        L.moe_workspace_query(_cfg(flags=L.MOE_FLAG_NO_STREAM | L.MOE_FLAG_STREAM_FC1), 128, 4096, 1.0)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARG
 
 
 def test_bf16_gateup_flag():
