@@ -11,21 +11,44 @@
 
 namespace moe {
 
-// One thread per (token, 8 consecutive columns).
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  const int chunks = a.hidden >> 3;
-  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (g >= (int64_t)a.tokens * chunks) return;
-  const int64_t t = g / chunks;
-  const int c = (int)(g - t * chunks) * 8;
-  combine8<false>(a.y, a.route_pos, a.staged_w, t, a.top_k, a.hidden, c, a.out);
+constexpr int kCombineThreads = 128;  // 8 columns each: 1024 columns of one token per workgroup
+
+// Workgroup b: token b / col_blocks, columns of its column block; one thread
+// per 8 consecutive columns.  The token is the same for the whole
+// workgroup, so its K positions and weights come through the scalar cache
+// (one load each per wave) and every vector load is a y row piece.
+template <int K>
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a, int col_blocks) {
+  const int b = (int)blockIdx.x;
+  const int t = b / col_blocks;
+  const int c = ((b - t * col_blocks) * kCombineThreads + (int)threadIdx.x) * 8;
+  typedef __attribute__((address_space(4))) const int32_t c_i32;
+  typedef __attribute__((address_space(4))) const float c_f32;
+  int pos[K];
+  float w[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    pos[k] = ((c_i32*)a.route_pos)[(int64_t)t * K + k];
+    w[k] = ((c_f32*)a.staged_w)[(int64_t)t * K + k];
+  }
+  if (c >= a.hidden) return;
+  combine8_pw<K, false>(a.y, pos, w, t, a.hidden, c, a.out);
 }
 
 int launch_combine(const CombineArgs& a, void* stream) {
   if (a.tokens <= 0) return 0;
-  const int64_t threads = (int64_t)a.tokens * (a.hidden / 8);
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), a);
+  const int col_blocks = (a.hidden / 8 + kCombineThreads - 1) / kCombineThreads;
+  if ((int64_t)a.tokens * col_blocks > 0x7fffffff) return -1;
+  const dim3 grid((unsigned)(a.tokens * col_blocks)), block(kCombineThreads);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (a.top_k) {
+    case 1: hipLaunchKernelGGL(combine_kernel<1>, grid, block, 0, s, a, col_blocks); break;
+    case 2: hipLaunchKernelGGL(combine_kernel<2>, grid, block, 0, s, a, col_blocks); break;
+    case 4: hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, s, a, col_blocks); break;
+    case 6: hipLaunchKernelGGL(combine_kernel<6>, grid, block, 0, s, a, col_blocks); break;
+    case 8: hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, s, a, col_blocks); break;
+    default: return -1;
+  }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

