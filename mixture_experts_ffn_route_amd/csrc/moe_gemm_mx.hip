@@ -493,8 +493,36 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
   }
 }
 
+// Token line layout of the ping-pong kernel: piece c of token t of a
+// 16-token area at position 8 t + (c ^ tok_swz(t)).
+__device__ __forceinline__ int tok_swz(int t) { return (t & 7) ^ ((t >> 3) & 1); }
+
+// Fragment whose "lo" and "hi" 16 bytes come from two per-lane addresses.
+__device__ __forceinline__ v8i lds_frag2(const lds_u8* lo_p, const lds_u8* hi_p) {
+  const u32x4 lo = *reinterpret_cast<lds_u32x4*>(lo_p);
+  const u32x4 hi = *reinterpret_cast<lds_u32x4*>(hi_p);
+  v8i r;
+  r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];
+  r[4] = (int)hi[0]; r[5] = (int)hi[1]; r[6] = (int)hi[2]; r[7] = (int)hi[3];
+  return r;
+}
+
+#include "moe_gemm_mx_pp.inc"
+
+// 128-token tiles without the fused combine run the ping-pong kernel.
 template <int BT, bool FC1>
 int launch_one(const MxGemmArgs& a, void* stream) {
+  if constexpr (BT == 128) {
+    if (a.fc.out == nullptr) {
+      if (a.w_e5m2)
+        hipLaunchKernelGGL((gemm_mx_pp_kernel<FC1, 1>), dim3(a.grid), dim3(kThreads), 0,
+                           static_cast<hipStream_t>(stream), a);
+      else
+        hipLaunchKernelGGL((gemm_mx_pp_kernel<FC1, 0>), dim3(a.grid), dim3(kThreads), 0,
+                           static_cast<hipStream_t>(stream), a);
+      return hipGetLastError() == hipSuccess ? 0 : -1;
+    }
+  }
   if (a.w_e5m2)
     hipLaunchKernelGGL((gemm_mx_kernel<BT, FC1, 1>), dim3(a.grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
                        a);
@@ -519,6 +547,11 @@ template <int BT, bool FC1>
 int occ() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_mx_kernel<BT, FC1, 0>, kThreads, 0) != hipSuccess) return 1;
+  if constexpr (BT == 128) {  // the grid serves either kernel: the smaller occupancy
+    int m = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, gemm_mx_pp_kernel<FC1, 0>, kThreads, 0) != hipSuccess) return 1;
+    n = m < n ? m : n;
+  }
   return n > 0 ? n : 1;
 }
 

@@ -62,6 +62,10 @@ CASES = [
     ("odd", None, False, 0.25),     # H = 384: the last 256-column slice is half full
     ("small", None, "e4m3", 0.25),  # MXFP8 x BF16 FC2
     ("odd", None, "e5m2", 0.0),
+    # 128-token MX tiles: the separate path runs the ping-pong MX kernels, the
+    # fused one the lockstep kernel at the same tile (odd: K of 3 and 2 blocks)
+    ("small", 4096, "e4m3", 0.25),
+    ("odd", 4096, "e5m2", 0.25),
 ]
 
 

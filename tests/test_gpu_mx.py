@@ -146,12 +146,13 @@ def test_mx_tactics_agree_bit_exact(expected_m, elem):
     assert np.array_equal(outs[0], outs[1])
 
 
+@pytest.mark.parametrize("expected_m", [48, 96])  # 64-token lockstep tiles; 128-token ping-pong tiles
 @pytest.mark.parametrize("tokens,elem", [(0, "e4m3"), (1, "e4m3"), (37, "e5m2"), (301, "e4m3"), (301, "e5m2")])
-def test_mx_ragged_token_counts(tokens, elem):
+def test_mx_ragged_token_counts(tokens, elem, expected_m):
     shape = MoEShape(512, 2048, 768, 32, 6, "topk")
     inp = _mx_inputs(shape, 4, elem)
     dev = to_device(inp)
-    layer = make_layer(shape, dev, expected_m=48, max_rows=512, mx=elem)
+    layer = make_layer(shape, dev, expected_m=expected_m, max_rows=512, mx=elem)
     out = run_forward(layer, dev, tokens=tokens)
     torch.cuda.synchronize()
     res = M.forward_mx(inp.x_bf16[:tokens], inp.topk_idx[:tokens], inp.topk_w[:tokens], inp.w13, inp.w13_scale,
