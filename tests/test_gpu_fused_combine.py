@@ -66,11 +66,18 @@ CASES = [
     # fused one the lockstep kernel at the same tile (odd: K of 3 and 2 blocks)
     ("small", 4096, "e4m3", 0.25),
     ("odd", 4096, "e5m2", 0.25),
+    ("k1_fc2", 4096, "e4m3", 0.0),  # I = 128: FC2 has one K-block per tile
+    ("k1_fc1", 4096, "e4m3", 0.0),  # H = 128: FC1 has one K-block per tile, FC2 one half-valid column tile
+    ("k1_fc2", 4096, False, 0.0),   # the same on the FP8 ping-pong kernels (256-token tiles)
+    ("k1_fc1", 4096, False, 0.0),
 ]
+
+_SHAPES = {"odd": MoEShape(40, 384, 256, 4, 2, "topk"), "k1_fc2": MoEShape(40, 384, 128, 4, 2, "topk"),
+           "k1_fc1": MoEShape(40, 128, 256, 4, 2, "topk")}
 
 
 def _shape(name):
-    return MoEShape(40, 384, 256, 4, 2, "topk") if name == "odd" else CONFIGS[name]
+    return _SHAPES[name] if name in _SHAPES else CONFIGS[name]
 
 
 @pytest.mark.parametrize("name,expected_m,mx,masked", CASES)
