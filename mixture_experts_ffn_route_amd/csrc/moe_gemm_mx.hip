@@ -68,6 +68,23 @@ __device__ __forceinline__ v8i lds_frag(const lds_u8* p) {
   return r;
 }
 
+// Token line layout in LDS: piece c (16 bytes) of token t of a 16-token
+// area at position 8 t + (c ^ tok_swz(t)).  One DMA instruction then fills
+// 8 whole 128-byte token lines (gathers of partial lines run at a fraction
+// of the L2 rate), and the fragment reads of 16 consecutive lanes hit 16
+// distinct 16-byte bank groups.
+__device__ __forceinline__ int tok_swz(int t) { return (t & 7) ^ ((t >> 3) & 1); }
+
+// Fragment whose "lo" and "hi" 16 bytes come from two per-lane addresses.
+__device__ __forceinline__ v8i lds_frag2(const lds_u8* lo_p, const lds_u8* hi_p) {
+  const u32x4 lo = *reinterpret_cast<lds_u32x4*>(lo_p);
+  const u32x4 hi = *reinterpret_cast<lds_u32x4*>(hi_p);
+  v8i r;
+  r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];
+  r[4] = (int)hi[0]; r[5] = (int)hi[1]; r[6] = (int)hi[2]; r[7] = (int)hi[3];
+  return r;
+}
+
 // LDS-DMA, explicit waits and a fence-free barrier, as in the FP8 kernel.
 __device__ __forceinline__ uint32_t lds_addr(const lds_u8* p) { return (uint32_t)(uintptr_t)p; }
 __device__ __forceinline__ void dma16(const uint8_t* src, const lds_u8* lds_wave_base) {
@@ -163,7 +180,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
   const int64_t rounds = (v_end - v_begin + per_xcd - 1) / per_xcd;
   const int stride = rounds > 0 ? (int)((v_end - v_begin + rounds - 1) / rounds) : per_xcd;
   const uint32_t a_lane = (uint32_t)(wn * C::NBH) * 2048u + (uint32_t)lane * 16u;
-  const uint32_t b_lane = (uint32_t)(wt * C::TBW) * 4096u + (uint32_t)lane * 16u;
+  // token fragment of lane (token tl, K-group q): pieces q and q + 4 of its
+  // token line (the scaled MFMA's K order: bytes 16q.. and 64 + 16q..)
+  const int tl = lane & 15, lq = lane >> 4;
+  const uint32_t b_lo = (uint32_t)(wt * C::TBW) * 4096u + 16u * (uint32_t)(8 * tl + (lq ^ tok_swz(tl)));
+  const uint32_t b_hi = (uint32_t)(wt * C::TBW) * 4096u + 16u * (uint32_t)(8 * tl + ((lq + 4) ^ tok_swz(tl)));
   const uint32_t bs_lane = (uint32_t)(wt * C::TBW * 64 + lane);
   // weight exponents: word group of the wave's first gate/first-half block,
   // and the byte of that block inside the word
@@ -206,15 +227,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
     const int64_t tile0 = ((int64_t)e * a.n_tiles + nt) * kbs;
     a_src = a.w + tile0 * C::A_BYTES + (wave * 4 * 64 + lane) * 16;
     as_src = a.w_scale + tile0 * 256 + wave * 32 + (lane < 32 ? lane : 0);
-    // activation terms: piece V of the wave covers LDS chunk V/64 = (token
-    // block, term, half); lane piece lp = (column group, token)
+    // activation terms: 2 KB per (token block, term), 16-byte piece c of
+    // token t at position 8 t + (c ^ tok_swz(t)), so that 8 consecutive
+    // lanes read one whole 128-byte token line; piece pv of the wave is
+    // position pv % 128 of area pv / 128
 #pragma unroll
     for (int j = 0; j < C::B_INSTR; ++j) {
       const int pv = wave * C::B_PIECES + j * 64 + (lane < C::B_LANES ? lane : 0);
-      const int c = pv >> 6, lp = pv & 63;
-      const int t = (c >> 2) * 16 + (lp & 15);
-      const int term = (c >> 1) & 1, half = c & 1;
-      b_src[j] = a.a + term * a.a_plane + src_row(t) * a.k_dim + 64 * half + 16 * (lp >> 4);
+      const int area = pv >> 7, pos = pv & 127;
+      const int tt = pos >> 3;
+      const int t = (area >> 1) * 16 + tt;
+      const int c = (pos & 7) ^ tok_swz(tt);
+      b_src[j] = a.a + (area & 1) * a.a_plane + src_row(t) * a.k_dim + 16 * c;
     }
     // activation exponents: word U covers token block U/64, lane U%64 =
     // token (U%16) and 32-block (U%64)/16
@@ -305,13 +329,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
       const lds_u8* Bs = As + C::A_BYTES + C::AS_BYTES;
       const lds_u32* BSs = (const lds_u32*)(Bs + C::B_BYTES);
       const lds_u8* Ap = As + a_lane;
-      const lds_u8* Bp = Bs + b_lane;
       v8i bh[C::TBW], bl[C::TBW];
       int sb[C::TBW];
 #pragma unroll
       for (int tb = 0; tb < C::TBW; ++tb) {
-        bh[tb] = lds_frag(Bp + tb * 4096);
-        bl[tb] = lds_frag(Bp + tb * 4096 + 2048);
+        bh[tb] = lds_frag2(Bs + b_lo + tb * 4096, Bs + b_hi + tb * 4096);
+        bl[tb] = lds_frag2(Bs + b_lo + tb * 4096 + 2048, Bs + b_hi + tb * 4096 + 2048);
         sb[tb] = (int)BSs[bs_lane + tb * 64];
       }
       const int sa_g = (int)(ASs[sa_grp * 64 + lane] >> sa_shift);
@@ -491,20 +514,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(MxGemmArgs a) {
       }
     }
   }
-}
-
-// Token line layout of the ping-pong kernel: piece c of token t of a
-// 16-token area at position 8 t + (c ^ tok_swz(t)).
-__device__ __forceinline__ int tok_swz(int t) { return (t & 7) ^ ((t >> 3) & 1); }
-
-// Fragment whose "lo" and "hi" 16 bytes come from two per-lane addresses.
-__device__ __forceinline__ v8i lds_frag2(const lds_u8* lo_p, const lds_u8* hi_p) {
-  const u32x4 lo = *reinterpret_cast<lds_u32x4*>(lo_p);
-  const u32x4 hi = *reinterpret_cast<lds_u32x4*>(hi_p);
-  v8i r;
-  r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];
-  r[4] = (int)hi[0]; r[5] = (int)hi[1]; r[6] = (int)hi[2]; r[7] = (int)hi[3];
-  return r;
 }
 
 #include "moe_gemm_mx_pp.inc"
