@@ -42,6 +42,12 @@ __device__ __forceinline__ void buffer_store8(st_u32x2 v, uint32_t voff, const s
 __device__ __forceinline__ void buffer_store16(st_u32x4 v, uint32_t voff, const st_u32x4& rsrc) {
   asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen\n\ts_nop 1" :: "v"(v), "v"(voff), "s"(rsrc) : "memory");
 }
+// The same, non-temporal: rows written once and read once much later (the
+// 256-token FC2 tiles' y rows, which at those token counts outgrow the
+// caches before the combine reads them).
+__device__ __forceinline__ void buffer_store16_nt(st_u32x4 v, uint32_t voff, const st_u32x4& rsrc) {
+  asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen nt\n\ts_nop 1" :: "v"(v), "v"(voff), "s"(rsrc) : "memory");
+}
 
 // A store that writes nothing (an empty buffer): it only counts as an
 // outstanding vector-memory operation.
