@@ -24,7 +24,7 @@ themselves; the weights carry block scale 1.  The promotion's final multiply
 (mantissa product 1/4, then 2^2) is then exact.
 
 The bound found here is the one the unfused gate/up check of
-``test_gpu_parity`` builds on (readings, MFMA accumulation).
+``test_gpu_parity`` builds on.
 """
 
 import math
