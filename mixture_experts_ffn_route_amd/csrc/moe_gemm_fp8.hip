@@ -365,11 +365,12 @@ static int launch_one(const GemmArgs& a, void* stream) {
   if constexpr (BT == kStreamBT) {
     if (a.stream_depth != 0) return launch_stream<FC1>(a, stream);
   }
-  if constexpr (BT == 256) {
-    // 256-token tiles: the ping-pong schedule (the tactic gives the variants
-    // with a gate/up output or the fused combine 128-token tiles)
+  if constexpr (BT == 256 || BT == 192) {
+    // 192- and 256-token tiles: the ping-pong schedule (the tactic gives the
+    // variants with a gate/up output or the fused combine 128-token tiles)
     if (a.gateup != nullptr || a.fc.out != nullptr) return -1;
-    hipLaunchKernelGGL((gemm_fp8_pp_kernel<FC1>), dim3(a.grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream), a);
+    hipLaunchKernelGGL((gemm_fp8_pp_kernel<FC1, BT>), dim3(a.grid), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), a);
   } else {
     hipLaunchKernelGGL((gemm_fp8_kernel<BT, FC1>), dim3(a.grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
                        a);
@@ -384,6 +385,7 @@ static int launch_bt(const GemmArgs& a, int block_m, void* stream) {
     case 32: return launch_one<32, FC1>(a, stream);
     case 64: return launch_one<64, FC1>(a, stream);
     case 128: return launch_one<128, FC1>(a, stream);
+    case 192: return launch_one<192, FC1>(a, stream);
     case 256: return launch_one<256, FC1>(a, stream);
   }
   return -1;
@@ -402,8 +404,8 @@ static int occ(int depth) {
                                                        kThreads, 0);
     else
       r = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_fp8_kernel<BT, FC1>, kThreads, 0);
-  } else if constexpr (BT == 256)
-    r = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_fp8_pp_kernel<FC1>, kThreads, 0);
+  } else if constexpr (BT == 256 || BT == 192)
+    r = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_fp8_pp_kernel<FC1, BT>, kThreads, 0);
   else
     r = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_fp8_kernel<BT, FC1>, kThreads, 0);
   if (r != hipSuccess) return 1;
@@ -418,6 +420,7 @@ int gemm_max_workgroups_per_cu(int which, int block_m, int stream_depth) {
     case 32: return f1 ? occ<32, true>(d) : occ<32, false>(d);
     case 64: return f1 ? occ<64, true>(d) : occ<64, false>(d);
     case 128: return f1 ? occ<128, true>(d) : occ<128, false>(d);
+    case 192: return f1 ? occ<192, true>(0) : occ<192, false>(0);
     default: return f1 ? occ<256, true>(0) : occ<256, false>(0);
   }
 }

@@ -99,6 +99,9 @@ Tactic choose_tactic(const moe_config_t& cfg, int32_t expected_m) {
                       (cfg.flags & (MOE_FLAG_UNFUSED_FC1 | MOE_FLAG_FUSED_COMBINE | MOE_FLAG_PERSISTENT_FFN));
   const int cap = cap128 ? 128 : 256;
   t.block_m = t.bucket <= 16 ? 16 : (t.bucket >= cap ? cap : t.bucket);
+  // 129-192 expected rows per expert: 192-token ping-pong tiles (one tile
+  // per expert with less padding than 256)
+  if (t.block_m == 256 && expected_m <= 192) t.block_m = 192;
   t.stages = t.block_m >= 256 ? 2 : (t.block_m >= 64 ? 3 : 4);
   if (is_mx(cfg.weight_format)) t.stages = t.block_m >= 128 ? 2 : (t.block_m >= 32 ? 3 : 4);
   return t;
