@@ -99,9 +99,15 @@ Tactic choose_tactic(const moe_config_t& cfg, int32_t expected_m) {
                       (cfg.flags & (MOE_FLAG_UNFUSED_FC1 | MOE_FLAG_FUSED_COMBINE | MOE_FLAG_PERSISTENT_FFN));
   const int cap = cap128 ? 128 : 256;
   t.block_m = t.bucket <= 16 ? 16 : (t.bucket >= cap ? cap : t.bucket);
-  // 129-192 expected rows per expert: 192-token ping-pong tiles (one tile
-  // per expert with less padding than 256)
-  if (t.block_m == 256 && expected_m <= 192) t.block_m = 192;
+  // 192-token ping-pong tiles where they pad an expert's expected rows at
+  // least 1/8 less than 256-token tiles (129-192 rows: one tile of 192, not
+  // of 256; 257-384: two of 192, not two of 256); the 256-token kernel does
+  // more per token, so near-equal padding keeps it.
+  if (t.block_m == 256) {
+    const int64_t m = expected_m;
+    const int64_t pad192 = (m + 191) / 192 * 192, pad256 = (m + 255) / 256 * 256;
+    if (pad192 * 8 < pad256 * 7) t.block_m = 192;
+  }
   t.stages = t.block_m >= 256 ? 2 : (t.block_m >= 64 ? 3 : 4);
   if (is_mx(cfg.weight_format)) t.stages = t.block_m >= 128 ? 2 : (t.block_m >= 32 ? 3 : 4);
   return t;
