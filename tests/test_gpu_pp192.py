@@ -3,9 +3,12 @@
 
 All tactics compute every output with the same operations in the same
 order, so the BF16 output, the FC1 codes and scales and the FC2 rows agree
-bit for bit across tile sizes.  The cases span ragged and masked tokens, a
-K of 3 and 2 blocks (each group's token scales then come from lanes of one
-wave only), a K of one block, and the DeepSeek-V3-like shape.
+bit for bit across tile sizes.  At 192 tokens a wave group holds 96 tokens: six
+token blocks per wave, three token DMA instructions per wave and K-block,
+the group's token scales from 64 + 32 lanes of two waves, and the
+promotion threads of rows 96-127 idle.  The cases span ragged and masked
+tokens, a K of 3 and 2 blocks, a K of one block, and the DeepSeek-V3-like
+shape.
 """
 
 import numpy as np
